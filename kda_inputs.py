@@ -1,0 +1,184 @@
+"""Seeded synthetic inputs for KDA prefill and decode.
+
+This module only draws random tensors with fixed laws and shapes.  It holds
+none of the recurrence's arithmetic, and both the HIP path's tests/benchmark
+and the fp64 oracle receive exactly the tensors it returns.
+
+Laws (one per workload; draws happen in the fixed order q, k, v, beta logits,
+log-alpha noise, initial state):
+
+* q, k ~ N(0, 1), each token-head vector scaled to unit L2 norm in fp32, then
+  cast to the working dtype (bf16 keeps the norm within about 2^-8 of 1).
+* v ~ N(0, 1), cast to the working dtype.
+* beta = sigmoid(N(0, 1)), fp32.
+* log_alpha, fp32, per (token, head, channel), one of
+    "softplus":  -min(softplus(N(0, 1)), 5)    values in [-5, 0)
+    "uniform53": U[-5, -3]                     pushed towards the -5 floor
+    "zero":      0                             no decay (alpha = 1)
+    "floor":     -5                            every channel at the floor
+* initial state ~ N(0, 0.02) (standard deviation 0.02), fp32, or zeros.
+* packed lengths: integers uniform on {lo, ..., hi}.
+
+Large tensors are drawn on the target device with a seeded torch generator so
+that 64K- and 1M-token workloads do not pass through host memory.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+LOG_ALPHA_LAWS = ("softplus", "uniform53", "zero", "floor")
+
+# Workloads, named by what they are.
+WORKLOADS = {
+    "tiny_fp32": dict(lengths=[256], H=2, d=64, dtype="f32", la_law="softplus", init="zeros", seed=0),
+    "bf16_4k": dict(lengths=[4096], H=96, d=128, dtype="bf16", la_law="softplus", init="normal", seed=1),
+    "varlen16": dict(lengths="uniform16_1k_8k", H=96, d=128, dtype="bf16", la_law="softplus", init="normal", seed=2),
+    "long_64k": dict(lengths=[65536], H=96, d=128, dtype="bf16", la_law="uniform53", init="normal", seed=3),
+    "long_1m": dict(lengths=[1048576], H=96, d=128, dtype="bf16", la_law="uniform53", init="normal", seed=3),
+}
+DECODE_WORKLOAD = dict(N=512, H=96, d=128, dtype="bf16", la_law="softplus", seed=4, steps=100)
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def varlen_lengths(seed: int, count: int = 16, lo: int = 1024, hi: int = 8192) -> list:
+    """Sequence lengths uniform on the integers {lo, ..., hi} (inclusive)."""
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(lo, hi + 1, size=count)]
+
+
+def workload_lengths(name: str) -> list:
+    spec = WORKLOADS[name]
+    if spec["lengths"] == "uniform16_1k_8k":
+        return varlen_lengths(spec["seed"])
+    return list(spec["lengths"])
+
+
+def _generator(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(int(seed))
+    return g
+
+
+def _unit_rows(x: torch.Tensor) -> torch.Tensor:
+    return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+
+
+def _log_alpha(shape, law: str, g: torch.Generator, device) -> torch.Tensor:
+    if law == "softplus":
+        z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        return -torch.clamp(torch.nn.functional.softplus(z), max=5.0)
+    if law == "uniform53":
+        u = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+        return -5.0 + 2.0 * u
+    if law == "zero":
+        return torch.zeros(shape, device=device, dtype=torch.float32)
+    if law == "floor":
+        return torch.full(shape, -5.0, device=device, dtype=torch.float32)
+    raise ValueError(f"unknown log-alpha law {law!r}")
+
+
+@dataclass
+class PrefillInputs:
+    q: torch.Tensor            # [T, H, d_k]  dtype
+    k: torch.Tensor            # [T, H, d_k]  dtype
+    v: torch.Tensor            # [T, H, d_v]  dtype
+    log_alpha: torch.Tensor    # [T, H, d_k]  fp32
+    beta: torch.Tensor         # [T, H]       fp32
+    init_state: Optional[torch.Tensor]   # [N, H, d_k, d_v] fp32 or None
+    cu_seqlens: Optional[torch.Tensor]   # [N + 1] int32 or None
+    lengths: list
+
+    @property
+    def N(self) -> int:
+        return len(self.lengths)
+
+
+def prefill_inputs(lengths: Sequence[int], H: int, d: int, dtype: str = "bf16",
+                   la_law: str = "softplus", init: str = "normal", seed: int = 0,
+                   device="cpu", d_v: Optional[int] = None, packed: Optional[bool] = None,
+                   slab: int = 65536) -> PrefillInputs:
+    """Draw one packed prefill batch.
+
+    ``packed`` controls whether ``cu_seqlens`` is returned (defaults to True
+    when there is more than one sequence).  Tensors are drawn in token slabs
+    of ``slab`` tokens to bound temporary memory on very long inputs.
+    """
+    d_k = d
+    d_v = d if d_v is None else d_v
+    lengths = [int(x) for x in lengths]
+    T = int(sum(lengths))
+    dt = torch_dtype(dtype)
+    g = _generator(seed, device)
+    q = torch.empty((T, H, d_k), dtype=dt, device=device)
+    k = torch.empty((T, H, d_k), dtype=dt, device=device)
+    v = torch.empty((T, H, d_v), dtype=dt, device=device)
+    beta = torch.empty((T, H), dtype=torch.float32, device=device)
+    la = torch.empty((T, H, d_k), dtype=torch.float32, device=device)
+    for t0 in range(0, T, slab):
+        t1 = min(T, t0 + slab)
+        n = t1 - t0
+        q[t0:t1] = _unit_rows(torch.randn((n, H, d_k), generator=g, device=device)).to(dt)
+        k[t0:t1] = _unit_rows(torch.randn((n, H, d_k), generator=g, device=device)).to(dt)
+        v[t0:t1] = torch.randn((n, H, d_v), generator=g, device=device).to(dt)
+        beta[t0:t1] = torch.sigmoid(torch.randn((n, H), generator=g, device=device))
+        la[t0:t1] = _log_alpha((n, H, d_k), la_law, g, device)
+    N = len(lengths)
+    if init == "normal":
+        init_state = 0.02 * torch.randn((N, H, d_k, d_v), generator=g, device=device)
+    elif init == "zeros":
+        init_state = None
+    else:
+        raise ValueError(f"unknown init law {init!r}")
+    if packed is None:
+        packed = N > 1
+    cu = None
+    if packed:
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device=device)
+    return PrefillInputs(q, k, v, la, beta, init_state, cu, lengths)
+
+
+def workload_inputs(name: str, device="cpu", **overrides) -> PrefillInputs:
+    spec = dict(WORKLOADS[name])
+    spec.update(overrides)
+    lengths = workload_lengths(name) if "lengths" not in overrides else overrides["lengths"]
+    return prefill_inputs(lengths, spec["H"], spec["d"], spec["dtype"], spec["la_law"],
+                          spec["init"], spec["seed"], device=device)
+
+
+def decode_state(N: int, H: int, d: int, seed: int, device="cpu", d_v: Optional[int] = None) -> torch.Tensor:
+    """Initial decode state [N, H, d_k, d_v] ~ N(0, 0.02), fp32."""
+    d_v = d if d_v is None else d_v
+    g = _generator(seed, device)
+    return 0.02 * torch.randn((N, H, d, d_v), generator=g, device=device)
+
+
+def decode_inputs(N: int, H: int, d: int, dtype: str = "bf16", la_law: str = "softplus",
+                  seed: int = 4, step: int = 0, device="cpu", d_v: Optional[int] = None) -> dict:
+    """Per-step decode inputs: q, k [N, H, d_k], v [N, H, d_v], log_alpha [N, H, d_k], beta [N, H]."""
+    d_v = d if d_v is None else d_v
+    dt = torch_dtype(dtype)
+    g = _generator(seed * 1_000_003 + 7919 * (step + 1), device)
+    q = _unit_rows(torch.randn((N, H, d), generator=g, device=device)).to(dt)
+    k = _unit_rows(torch.randn((N, H, d), generator=g, device=device)).to(dt)
+    v = torch.randn((N, H, d_v), generator=g, device=device).to(dt)
+    beta = torch.sigmoid(torch.randn((N, H), generator=g, device=device))
+    la = _log_alpha((N, H, d), la_law, g, device)
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta)
+
+
+def to_numpy(x: Optional[torch.Tensor]):
+    """Exact host copy: bf16 is widened to fp32 (exactly), fp32 is copied as is."""
+    if x is None:
+        return None
+    x = x.detach().to("cpu")
+    if x.dtype == torch.bfloat16:
+        x = x.float()
+    return x.numpy()

@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for Kimi Delta Attention -- test infrastructure only.
+
+Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this package.  The HIP library never does.
+"""
+from .kda_oracle import kda_decode_step, kda_prefill, kda_recurrence
+
+__all__ = ["kda_prefill", "kda_decode_step", "kda_recurrence"]
