@@ -1,0 +1,166 @@
+"""ctypes binding of libkda.so.
+
+Marshalling only: tensors are checked for device, dtype, shape and layout,
+outputs are allocated with torch when the caller does not pass them, and the
+C entry points of the same names are called with raw device pointers and the
+caller's current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no fallback of any kind.  When the library is missing or
+cannot be loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK = 0
+KDA_F32 = 0
+KDA_BF16 = 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_NO_DEVICE", 6: "KDA_ERR_HIP"}
+
+# Every symbol include/kda.h declares, with its ctypes signature.
+_VP, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+SIGNATURES = {
+    "kda_abi_version": (ctypes.c_int, []),
+    "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kda_last_error": (ctypes.c_char_p, []),
+    "kda_chunk_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
+                                          _VP, _VP, _VP]),
+    "kda_decode_step": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP,
+                                        _I32, _I32, _I32, _I32, ctypes.c_int, _VP, _VP]),
+}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = _lib
+        detail = ""
+        if lib is not None:
+            detail = lib.kda_status_string(status).decode()
+            last = lib.kda_last_error().decode()
+            if last:
+                detail += f" ({last})"
+        super().__init__(f"{fn} returned {_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def load(path: Optional[str] = None):
+    """Load libkda.so (once) and declare its signatures.  Raises if it is absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run `python -m gated_delta_rule_09_amd.build` first")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.kda_abi_version() != 1:
+        raise RuntimeError("libkda ABI version mismatch")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {dt}")
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      log_alpha: torch.Tensor, beta: torch.Tensor,
+                      init_state: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None,
+                      o: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None,
+                      output_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill; see include/kda.h.  Returns (o, final_state)."""
+    lib = load()
+    T, H, d_k = q.shape
+    d_v = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(k, "k", (T, H, d_k), dt, dev)
+    _check(v, "v", (T, H, d_v), dt, dev)
+    _check(log_alpha, "log_alpha", (T, H, d_k), torch.float32, dev)
+    _check(beta, "beta", (T, H), torch.float32, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (N, H, d_k, d_v), torch.float32, dev)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((T, H, d_v), dtype=dt, device=dev)
+    _check(o, "o", (T, H, d_v), dt, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, d_k, d_v), torch.float32, dev)
+    st = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                               _ptr(init_state), _ptr(cu_seqlens), N, T, H, d_k, d_v, code,
+                               _ptr(o), _ptr(final_state), _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_chunk_prefill", st)
+    return o, final_state
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    log_alpha: torch.Tensor, beta: torch.Tensor, state: torch.Tensor,
+                    o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One KDA decode step; ``state`` is updated in place.  Returns o [N, H, d_v]."""
+    lib = load()
+    N, H, d_k = q.shape
+    d_v = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(q, "q", (N, H, d_k), dt, dev)
+    _check(k, "k", (N, H, d_k), dt, dev)
+    _check(v, "v", (N, H, d_v), dt, dev)
+    _check(log_alpha, "log_alpha", (N, H, d_k), torch.float32, dev)
+    _check(beta, "beta", (N, H), torch.float32, dev)
+    _check(state, "state", (N, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, d_v), dtype=dt, device=dev)
+    _check(o, "o", (N, H, d_v), dt, dev)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state),
+                             N, H, d_k, d_v, code, _ptr(o), _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_decode_step", st)
+    return o

@@ -1,0 +1,129 @@
+// C ABI of libkda: host-side argument validation and dispatch to the kernels.
+// Every validation failure returns before any HIP runtime call.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char* what, hipError_t e) {
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_d(int32_t d) { return d == 64 || d == 128; }
+
+// gfx950 check, cached per device id.
+constexpr int kMaxDevices = 64;
+int g_arch_ok[kMaxDevices];      // 0 unknown, 1 ok, -1 not gfx950
+std::mutex g_arch_mu;
+
+kda_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) {
+        set_error("hipGetDevice", e);
+        (void)hipGetLastError();
+        return KDA_ERR_NO_DEVICE;
+    }
+    if (dev >= kMaxDevices) return KDA_ERR_NO_DEVICE;
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_arch_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) {
+            set_error("hipGetDeviceProperties", e);
+            (void)hipGetLastError();
+            return KDA_ERR_NO_DEVICE;
+        }
+        g_arch_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+        if (g_arch_ok[dev] < 0)
+            snprintf(g_last_error, sizeof(g_last_error), "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    }
+    return g_arch_ok[dev] > 0 ? KDA_OK : KDA_ERR_NO_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "unsupported or inconsistent sizes";
+        case KDA_ERR_DTYPE: return "unsupported dtype";
+        case KDA_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case KDA_ERR_NO_DEVICE: return "no usable gfx950 HIP device";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           float* state, int32_t N, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype dtype,
+                           void* o, void* stream) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (N < 0 || H < 1 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
+        !aligned16(beta) || !aligned16(state) || !aligned16(o))
+        return KDA_ERR_ALIGN;
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    kda::DecodeArgs a{q, k, v, log_alpha, beta, state, o, N, H, d_k, d_v,
+                      dtype == KDA_BF16, reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = kda::launch_decode(a);
+    if (e != hipSuccess) {
+        set_error("kda_decode_step launch", e);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta,
+                             const float* init_state, const int32_t* cu_seqlens,
+                             int32_t N, int64_t total_T, int32_t H,
+                             int32_t d_k, int32_t d_v, kda_dtype dtype,
+                             void* o, float* final_state, void* stream) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (N < 1 || H < 1 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
+    if (dtype == KDA_F32 && d_k != 64) return KDA_ERR_SHAPE;
+    if (cu_seqlens == nullptr && N != 1) return KDA_ERR_SHAPE;
+    if (N > 65535 || H > 65535) return KDA_ERR_SHAPE;   // grid dimensions
+    if ((int64_t)N * H > (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
+    if (total_T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    if (total_T == 0 && final_state == nullptr) return KDA_OK;
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    kda::PrefillArgs a{q, k, v, log_alpha, beta, init_state, cu_seqlens, N, total_T, H, d_k, d_v,
+                       dtype == KDA_BF16, o, final_state, reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = kda::launch_prefill(a);
+    if (e != hipSuccess) {
+        set_error("kda_chunk_prefill launch", e);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// KDA single-token decode: one read-modify-write pass over each fp32 state.
+//
+// For one (sequence, head) the recurrence of "Kimi K3 -- Architecture Notes"
+// section 1.1 applied to a single token is rearranged as
+//     a  = exp(log_alpha)                       (retention, per key channel c)
+//     e  = S^T (a * k)      o' = S^T (a * q)    (two reductions over c)
+//     w  = beta (v - e)
+//     o  = o' + w (k^T q)
+//     S <- Diag(a) S + k w^T
+// so the state is read once and written once: the kernel is HBM-bound
+// (2 * d_k * d_v * 4 bytes per pair against ~7 d_k d_v flops).
+//
+// One 256-thread workgroup per pair.  Thread t owns a 4-column slice
+// (columns 4*(t % (DV/4)) .. +3) of ROWS state rows, rows interleaved so that
+// each load instruction of a wave covers whole adjacent rows (coalesced
+// 16-byte accesses).  The state slice stays in registers between the read and
+// the write.
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    float* __restrict__ state, T* __restrict__ o, int64_t pairs) {
+    constexpr int NT = 256;
+    constexpr int QUADS = DV / 4;          // threads per state row
+    constexpr int RG = NT / QUADS;         // row groups
+    constexpr int ROWS = DK / RG;          // rows per thread
+    static_assert(DK % RG == 0, "shape");
+
+    __shared__ float s_a[DK], s_ak[DK], s_aq[DK], s_k[DK];
+    __shared__ f32x4 s_red[2][RG][QUADS];
+    __shared__ float s_w[DV];
+    __shared__ float s_kq[NT / kWave];
+
+    const int64_t pair = blockIdx.x;
+    if (pair >= pairs) return;
+    const int t = threadIdx.x;
+    const int vq = t % QUADS;
+    const int rg = t / QUADS;
+
+    float* S = state + pair * (int64_t)(DK * DV);
+
+    // Issue the state loads first: they are the bulk of the traffic.
+    f32x4 s[ROWS];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int row = i * RG + rg;
+        s[i] = *reinterpret_cast<const f32x4*>(S + row * DV + 4 * vq);
+    }
+
+    // Per-channel vectors.
+    float kq_part = 0.f;
+    if (t < DK) {
+        const float a = __expf(log_alpha[pair * DK + t]);
+        const float kk = Elem<T>::load(k, pair * DK + t);
+        const float qq = Elem<T>::load(q, pair * DK + t);
+        s_a[t] = a;
+        s_ak[t] = a * kk;
+        s_aq[t] = a * qq;
+        s_k[t] = kk;
+        kq_part = kk * qq;
+    }
+    kq_part = wave_sum(kq_part);
+    if ((t % kWave) == 0) s_kq[t / kWave] = kq_part;
+    __syncthreads();
+
+    // Partial reductions over this thread's rows.
+    f32x4 e = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int row = i * RG + rg;
+        e += s[i] * s_ak[row];
+        op += s[i] * s_aq[row];
+    }
+    s_red[0][rg][vq] = e;
+    s_red[1][rg][vq] = op;
+    __syncthreads();
+
+    if (t < DV) {
+        const int cq = t / 4, cl = t % 4;
+        float es = 0.f, os = 0.f;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            es += s_red[0][g][cq][cl];
+            os += s_red[1][g][cq][cl];
+        }
+        float kq = 0.f;
+#pragma unroll
+        for (int i = 0; i < NT / kWave; ++i) kq += s_kq[i];
+        const float w = beta[pair] * (Elem<T>::load(v, pair * DV + t) - es);
+        s_w[t] = w;
+        Elem<T>::store(o, pair * DV + t, os + w * kq);
+    }
+    __syncthreads();
+
+    const f32x4 w4 = {s_w[4 * vq], s_w[4 * vq + 1], s_w[4 * vq + 2], s_w[4 * vq + 3]};
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int row = i * RG + rg;
+        const f32x4 nv = s[i] * s_a[row] + s_k[row] * w4;
+        *reinterpret_cast<f32x4*>(S + row * DV + 4 * vq) = nv;
+    }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+    const int64_t pairs = (int64_t)a.N * a.H;
+    if (pairs == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)pairs), dim3(256), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.state,
+                       (T*)a.o, pairs);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_decode_dtype(const DecodeArgs& a) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_decode_t<T, 128, 128>(a);
+    if (a.d_k == 128 && a.d_v == 64) return launch_decode_t<T, 128, 64>(a);
+    if (a.d_k == 64 && a.d_v == 128) return launch_decode_t<T, 64, 128>(a);
+    return launch_decode_t<T, 64, 64>(a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+    return a.bf16 ? launch_decode_dtype<uint16_t>(a) : launch_decode_dtype<float>(a);
+}
+
+}  // namespace kda

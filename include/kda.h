@@ -1,0 +1,142 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * The operation (one head; "Kimi K3 -- Architecture Notes", section 1.1):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * with S in R^{d_k x d_v} (the fixed-size state of the same section),
+ * alpha_t = exp(log_alpha_t) in (0,1]^{d_k} a per-channel retention factor acting
+ * on the d_k rows of S, and beta_t in [0,1] the write strength.  There is no
+ * 1/sqrt(d_k) output scale.
+ *
+ * Memory layout (all arrays dense, row-major, innermost index last):
+ *     q, k        [T, H, d_k]        element type given by `dtype`
+ *     v           [T, H, d_v]        element type given by `dtype`
+ *     log_alpha   [T, H, d_k]        float32
+ *     beta        [T, H]             float32
+ *     state       [N, H, d_k, d_v]   float32 (row index = key channel)
+ *     o           [T, H, d_v]        element type given by `dtype`
+ * For decode, T is replaced by N (one token per sequence).
+ *
+ * Ownership: every pointer is caller-owned device memory (any allocation the
+ * HIP runtime can address from the current device).  The library neither
+ * frees nor retains pointers after a call returns and allocates no device
+ * memory of its own.
+ *
+ * Asynchrony: calls validate their arguments on the host, enqueue kernels on
+ * `stream` (a hipStream_t; NULL = the legacy default stream) and return; the
+ * outputs are valid once the stream has been synchronised.
+ *
+ * Errors: host-side validation failures return a non-zero kda_status BEFORE any
+ * HIP call is made.  A failed kernel launch returns KDA_ERR_HIP.  Errors raised
+ * asynchronously by an earlier kernel surface as KDA_ERR_HIP on a later call or
+ * on the caller's own synchronisation.  The library never aborts and never
+ * lets an exception cross this interface.
+ *
+ * Value preconditions that are documented but not checked (checking them
+ * would need an extra pass over device memory):
+ *     log_alpha in [-5, 0]  (the lower bound of section 1.2 of the notes; the
+ *                            prefill kernel relies on it to keep every
+ *                            16-token rescale factor within e^80),
+ *     beta in [0, 1], and q, k of unit L2 norm per token-head (section 1.1).
+ * cu_seqlens is clamped on the device into [0, total_T] and made
+ * non-decreasing, so malformed offsets cannot cause out-of-range accesses;
+ * they do produce meaningless output.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,       /* a required pointer is NULL                        */
+    KDA_ERR_SHAPE = 2,      /* unsupported or inconsistent sizes                 */
+    KDA_ERR_DTYPE = 3,      /* dtype is not one of kda_dtype                     */
+    KDA_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned                  */
+    KDA_ERR_NO_DEVICE = 5,  /* no HIP device, or the current device is not gfx950 */
+    KDA_ERR_HIP = 6         /* a HIP runtime call failed                          */
+} kda_status;
+
+typedef enum {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/* Version of this interface; bumped on any incompatible change. */
+#define KDA_ABI_VERSION 1
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Text of the last HIP error seen by the library on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/*
+ * kda_chunk_prefill -- KDA over a packed batch of N sequences.
+ *
+ * Implements the section-1.1 recurrence chunkwise: "recurrent across chunks and
+ * parallel within each chunk" (section 1.2 of the notes), with 64-token chunks
+ * split into 16-token tiles whose decay is taken relative to the tile start in
+ * log space.  The result equals the token-by-token recurrence up to rounding.
+ *
+ *   q, k, v, log_alpha, beta : inputs, layouts above, total_T tokens.
+ *   init_state  : [N, H, d_k, d_v] fp32 initial state per sequence, or NULL for
+ *                 zeros.  May alias final_state (each sequence reads its slab
+ *                 before writing it).
+ *   cu_seqlens  : device int32 [N + 1]; sequence n owns tokens
+ *                 [cu_seqlens[n], cu_seqlens[n+1]).  Requires cu[0] = 0,
+ *                 non-decreasing, cu[N] = total_T.  NULL means N must be 1 and
+ *                 the single sequence covers all total_T tokens.
+ *                 Zero-length sequences are allowed (final = init).
+ *   N           : number of sequences, >= 1.
+ *   total_T     : total tokens, >= 0 (0 copies init to final).
+ *   H           : heads, >= 1.
+ *   d_k, d_v    : 64 or 128 each.  dtype KDA_F32 requires d_k = 64.
+ *   dtype       : element type of q, k, v and o.  The state is always fp32.
+ *   o           : [total_T, H, d_v] output (required when total_T > 0).
+ *   final_state : [N, H, d_k, d_v] fp32 output, or NULL to skip storing it.
+ *   stream      : hipStream_t to enqueue on.
+ */
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta,
+                             const float* init_state, const int32_t* cu_seqlens,
+                             int32_t N, int64_t total_T, int32_t H,
+                             int32_t d_k, int32_t d_v, kda_dtype dtype,
+                             void* o, float* final_state, void* stream);
+
+/*
+ * kda_decode_step -- advance N independent sequences by one token each.
+ *
+ * Per (sequence, head) one pass over the state: with a = exp(log_alpha),
+ *     w  = beta (v - S^T (a * k)),
+ *     o  = S^T (a * q) + w (k^T q),
+ *     S <- Diag(a) S + k w^T            (written back in place),
+ * which is the section-1.1 recurrence for a single token, rearranged so that S
+ * is read once and written once.
+ *
+ *   q, k, v, log_alpha, beta : [N, H, d_k] / [N, H, d_v] / [N, H, d_k] / [N, H].
+ *   state  : [N, H, d_k, d_v] fp32, read and overwritten in place.
+ *   N, H   : >= 1 (N = 0 is a no-op).  d_k, d_v: 64 or 128.
+ *   dtype  : element type of q, k, v and o.
+ *   o      : [N, H, d_v] output.
+ *   stream : hipStream_t to enqueue on.
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           float* state, int32_t N, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype dtype,
+                           void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */
