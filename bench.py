@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunkwise prefill of the long-context workload (one sequence,
+T = 65,536 tokens, H = 96 heads, d_k = d_v = 128, bf16 q/k/v, fp32 log-decay
+and beta, fp32 state) followed by one decode step of the batched-decode
+workload (512 sequences x 96 heads, fp32 state of 3.2 GB updated in place).
+Inputs are synthetic, seeded, and resident in device memory before timing.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is prefill tokens/s; decode state-update
+bandwidth is reported under "decode".  Kernel durations come from HIP events
+recorded on the stream the kernels are launched on.
+"""
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
+
+T_PREFILL, H, D = 65536, 96, 128
+N_DECODE = 512
+# Algorithmic bytes (bf16 q/k/v, fp32 log-decay, fp32 beta, bf16 o).
+PREFILL_BYTES_PER_TOKEN_HEAD = 3 * D * 2 + D * 4 + 4 + D * 2          # 1540
+STATE_BYTES = D * D * 4                                                  # 64 KiB
+DECODE_BYTES_PER_PAIR = 2 * STATE_BYTES + 3 * D * 2 + D * 4 + 4 + D * 2  # 132,612
+# Algorithmic flops per token-head, chunk 64, causal triangles only.
+PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 2 * 64 * (D + D)              # 131,072
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the prefill
+    workload: 8 heads of the 64K-token sequence, consecutive 1024-token
+    segments with the state carried, until the time budget is spent.  Runs in
+    a single-threaded subprocess so that `cores` is exact."""
+    code = r"""
+import json, sys, time
+sys.path.insert(0, %r)
+import numpy as np
+import kda_inputs as ki
+import oracle
+x = ki.prefill_inputs([65536], H=8, d=%d, dtype="bf16", la_law="uniform53", init="normal", seed=3)
+n = ki.to_numpy
+q, k, v, la, b, S = (n(x.q), n(x.k), n(x.v), n(x.log_alpha), n(x.beta), n(x.init_state)[0].astype(np.float64))
+done, t0 = 0, time.perf_counter()
+while done < q.shape[0]:
+    sl = slice(done, done + 1024)
+    _, S = oracle.kda_recurrence(q[sl], k[sl], v[sl], la[sl], b[sl], S)
+    done += 1024
+    if time.perf_counter() - t0 > %f:
+        break
+dt = time.perf_counter() - t0
+print(json.dumps({"token_heads": done * 8, "seconds": dt}))
+""" % (ROOT, D, budget_s)
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
+    if out.returncode != 0:
+        raise RuntimeError(out.stderr[-2000:])
+    r = json.loads(out.stdout.strip().splitlines()[-1])
+    th_per_s = r["token_heads"] / r["seconds"]
+    return {"value": th_per_s / H, "unit": "tokens/s (H=96 equivalent)", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 oracle, 8 heads x {r['token_heads'] // 8} tokens of the 64K prefill workload "
+                      f"({r['seconds']:.1f} s, {th_per_s:.0f} token-heads/s, single thread)"}
+
+
+def measured_traffic(kernel: str, launch_ms: float):
+    """HBM bytes per launch measured by the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes (calibrated against a plain copy), as GB/s over this run's launch
+    time; None when the kernel's source changed since the counters were
+    taken or no measurement is stored."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+            return None
+    return round((rec["hbm_bytes_read"] + rec["hbm_bytes_written"]) / (launch_ms * 1e-3) / 1e9, 1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="also run one plain device-to-device copy of this many GiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
+                                   "this build (--gpus must be 1)"}))
+        sys.exit(2)
+
+    import torch
+    import kda_inputs as ki
+    from gated_delta_rule_09_amd import kda_chunk_prefill, kda_decode_step
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = ki.workload_inputs("long_64k", device=dev)
+    o = torch.empty_like(x.v)
+    fin = torch.empty_like(x.init_state)
+    w = ki.DECODE_WORKLOAD
+    state = ki.decode_state(w["N"], w["H"], w["d"], seed=w["seed"], device=dev)
+    dx = ki.decode_inputs(w["N"], w["H"], w["d"], dtype=w["dtype"], la_law=w["la_law"], seed=w["seed"], step=0,
+                          device=dev)
+    od = torch.empty_like(dx["v"])
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kda_chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state, None, o=o, final_state=fin)
+        if ev is not None:
+            ev[1].record(stream)
+        kda_decode_step(dx["q"], dx["k"], dx["v"], dx["log_alpha"], dx["beta"], state, o=od)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    if args.calibrate_copy_gib > 0:
+        nbytes = int(args.calibrate_copy_gib * (1 << 30))
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    pre_bytes = T_PREFILL * H * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * H * STATE_BYTES
+    pre_gbps = pre_bytes / (pre_ms * 1e-3) / 1e9
+    pre_tflops = T_PREFILL * H * PREFILL_FLOPS_PER_TOKEN_HEAD / (pre_ms * 1e-3) / 1e12
+    dec_bytes = N_DECODE * H * DECODE_BYTES_PER_PAIR
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    tok_s = T_PREFILL / (pre_ms * 1e-3)
+
+    res = {
+        "metric": "KDA prefill tokens/s (H=96,d=128,T=64K) + decode state-update HBM GB/s",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_prefill T=65536 H=96 d=128 bf16 (log-decay U[-5,-3], fp32 state) "
+                               "+ kda_decode_step N=512 H=96 d=128 bf16 (fp32 state 3.2 GB in place)",
+                   "prefill_tokens": T_PREFILL, "heads": H, "d_k": D, "d_v": D, "chunk": 64,
+                   "decode_sequences": N_DECODE},
+        "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("prefill", pre_ms),
+                     "kernel": "prefill_kernel", "avg_launch_ms": round(pre_ms, 4),
+                     "algorithmic_bytes_per_launch": pre_bytes,
+                     "mfma_frac_algorithmic": round(pre_tflops / BF16_DENSE_PEAK_TFLOPS, 4)},
+        "decode": {"gbps": round(dec_gbps, 1), "ms_per_step": round(dec_ms, 4),
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                                "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                                "traffic": measured_traffic("decode", dec_ms),
+                                "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec_bytes}},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
