@@ -3,56 +3,52 @@
 // The recurrence of "Kimi K3 -- Architecture Notes", section 1.1,
 //     S_t = (I - b_t k_t k_t^T) Diag(alpha_t) S_{t-1} + b_t k_t v_t^T,  o_t = S_t^T q_t,
 // is evaluated "recurrent across chunks and parallel within each chunk"
-// (section 1.2).  For a chunk of C = 64 tokens starting from state S0, with
-// g_r = sum_{s<=r} log alpha_s (per key channel) and Gamma_r = exp(g_r):
+// (section 1.2).  Tokens are streamed in chunks of 64, and each chunk is cut
+// into four 16-token tiles ("secondary tiles", section 1.2).  The state is
+// carried from tile to tile.  For one tile of positions r = 1..16 starting from
+// state S (d_k x d_v), with x_r = sum_{s<=r} log2-decay (per key channel),
+// X = x_16, e1_r = 2^{x_r}, e2_r = 2^{X - x_r}:
 //
-//   M_rs = sum_c k_rc k_sc e^{g_rc - g_sc}   (s < r)     decayed key Gram
-//   P_rs = sum_c q_rc k_sc e^{g_rc - g_sc}   (s <= r)    decayed query-key Gram
-//   W    = (I + Diag(b) M)^{-1} Diag(b) (V - K_Gamma S0) pseudo-values, K_Gamma = K * Gamma
-//   O    = Q_Gamma S0 + P W                              chunk output, Q_Gamma = Q * Gamma
-//   S    = Diag(Gamma_C) S0 + (K * Gamma_C / Gamma)^T W  next chunk's state
+//   P_rs = sum_c q_rc e1_rc * k_sc 2^{-x_sc}       (s <= r)   decayed query-key Gram
+//   M_rs = sum_c k_rc e1_rc * k_sc 2^{-x_sc}       (s <  r)   decayed key Gram
+//   A    = (I + Diag(b) M)^{-1} Diag(b)                      unit-lower-triangular solve
+//   W    = A (V - (K * e1) S)                                pseudo-values
+//   O    = (Q * e1) S + P W                                  tile output
+//   S   <- Diag(2^X) S + (K * e2)^T W                        state after the tile
 //
-// which follows from unrolling the recurrence inside the chunk: the delta
-// correction of token r sees the decayed state and the corrections of the
-// chunk's earlier tokens, which gives the unit-lower-triangular system.  The
-// system is solved by blocks of 16 tokens: with A_ii = (I + Diag(b_i) M_ii)^{-1}
-// Diag(b_i) for the four diagonal blocks,
-//   W_i = A_ii (U_i - sum_{j<i} M_ij W_j),   U = V - K_Gamma S0.
+// which is the token recurrence regrouped exactly: the delta correction of
+// token r sees the decayed state and the corrections of the tile's earlier
+// tokens, which gives the triangular system.
 //
-// Range control (section 1.2 of the notes): every factor e^{g_r - g_s} with
-// s <= r is at most 1, but splitting it into a row part and a column part for a
-// matrix product needs a reference point.  The chunk is cut into four 16-token
-// tiles; tile i has reference rho_i = g just before the tile.  Because
-// log alpha >= -5, a tile's cumulative log-decay lies in [-80, 0], so
-//   row factor    e^{g_r - rho_i}        in [e^-80, 1]
-//   column factor e^{rho_i - g_s}        in [1, e^80]   (s in the same tile)
-//                                        in [0, 1]      (s in an earlier tile)
-// all representable in fp32 and bf16 (8-bit exponent).  Every tile pair,
-// diagonal or not, is then a dense MFMA product.  Decay arithmetic runs in
-// base 2 (log alpha * log2 e) so that v_exp_f32 is used directly; within a
-// tile the factors are running products of alpha (one exponential per
-// element), across tiles they come from sums of log alpha.
+// Range control (section 1.2 of the notes): log alpha >= -5, so within a
+// 16-token tile x lies in [-115.4, 0] (base 2, i.e. [-80, 0] in base e):
+// e1, e2 lie in [2^-115, 1] and the column factor 2^{-x} in [1, 2^115], all
+// representable in fp32 and bf16 (8-bit exponent).  Every factor is a running
+// product of alpha = 2^{log2-decay} within the tile (one v_exp_f32 per
+// element); no pairwise exponentials are needed and no factor spans more than
+// one tile.
 //
-// Work decomposition: one workgroup of NW waves per (sequence, head, V-block
-// of BV = 16 NW value columns); the recurrence is independent across value
-// columns.  Per chunk:
-//   E  elementwise: per-tile decay factors and scaled operands, written to LDS
-//      row-major with the contraction index contiguous.  Thread = (tile,
-//      channels), so the running products are sequential in registers;
-//   G  the P and M tile products (MFMA, row fragments reused across columns);
-//   S  the four diagonal 16x16 inverses, fp32 right-looking substitution;
-//   SD the state-dependent part, wave-local: wave w owns value columns
-//      16w .. 16w+15.  Its slab of S, and U and W, live in MFMA accumulators
-//      and are fed back directly as MFMA operands (an accumulator tile holds 4
-//      consecutive rows per lane, exactly the K-layout of an operand); the
-//      LDS operands are read with the matching row permutation.  No LDS writes
-//      and no barriers inside SD.
-// The global loads of chunk c+1 are issued while chunk c is being processed.
+// Work decomposition: one workgroup of four waves per (sequence, head, block of
+// 64 value columns); the recurrence is independent across value columns.  Per
+// 64-token chunk two independent halves run in the same iteration:
+//   SI  (state-independent, chunk c+1): wave i owns tile i.  It forms the tile's
+//       decay factors and scaled operands, the tile's P and M (MFMA) and the
+//       16x16 inverse (fp32 substitution), and writes them to one of two LDS
+//       buffers.  Thread = (tile, two key channels): the running products are
+//       sequential in registers.
+//   SD  (state-dependent, chunk c): wave w owns value columns 16w .. 16w+15 and
+//       walks the chunk's four tiles.  Its slab of S, and U and W, live in MFMA
+//       accumulators and are fed back as MFMA operands directly (an accumulator
+//       tile holds 4 consecutive rows per lane, the K-layout of an operand);
+//       the LDS operands are read with the matching row permutation.
+// One barrier per chunk hands the SI buffer to SD.  Global loads run one chunk
+// ahead.  The two value-column workgroups of a head are placed 8 workgroups
+// apart so that they land on the same XCD and share its L2.
 //
-// Operand precision: bf16 inputs use bf16 MFMA operands with fp32
-// accumulation (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16); fp32 inputs use
-// v_mfma_f32_16x16x4_f32.  The state, the decay arithmetic and the diagonal
-// inverses are fp32 throughout.
+// Operand precision: bf16 inputs use bf16 MFMA operands with fp32 accumulation
+// (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16); fp32 inputs use
+// v_mfma_f32_16x16x4_f32.  The state, the decay arithmetic and the inverse are
+// fp32 throughout.
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -61,27 +57,35 @@ namespace kda {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kC = 64;        // chunk length
+constexpr int kC = 64;        // chunk length (tokens per pipeline step)
 constexpr int kTiles = 4;     // 16-token tiles per chunk
+constexpr int kNW = 4;        // waves per workgroup
+constexpr int kBV = 16 * kNW; // value columns per workgroup
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Order this wave's earlier LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // MFMA helpers.  Accumulator layout (CDNA 16x16): lane l, register e holds
-// D[4*(l/16) + e][l % 16].  Below, "acc tile" X is such a 16x16 fp32 tile and
-// "row of an LDS operand" is a pointer to the 16-wide K segment of the row
-// that this lane's M (or N) index selects.  Every product pairs, for lane
-// group g = l/16 and slot e, row 4g+e of the accumulator tile with column
-// 4g+e of the LDS row, so the contraction is complete whatever order the
-// hardware assigns to K.
+// D[4*(l/16) + e][l % 16].  An "acc tile" X is such a 16x16 fp32 tile; an "LDS
+// row" is a pointer to the 16-wide K segment of the row that this lane's M (or
+// N) index selects.  Every product pairs, for lane group g = l/16 and slot e,
+// row 4g+e of the accumulator tile with column 4g+e of the LDS row, so the
+// contraction is complete whatever order the hardware assigns to K.
 // ---------------------------------------------------------------------------
 template <typename OT> struct Op;
 
 template <> struct Op<uint16_t> {    // bf16 operands
-    static constexpr int KS = 32;    // K of the LDS x LDS product
+    static constexpr int KS = 32;    // K of an LDS x LDS product step
     typedef bf16x8 Frag;
+    typedef u32x2 Xop;               // an acc tile as a bf16 operand (4 values)
     static __device__ __forceinline__ Frag frag(const uint16_t* base, int ld, int k0) {
         const int lane = threadIdx.x & 63;
         return *reinterpret_cast<const bf16x8*>(base + (lane & 15) * ld + 8 * (lane >> 4) + k0);
@@ -89,24 +93,24 @@ template <> struct Op<uint16_t> {    // bf16 operands
     static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
-    static __device__ __forceinline__ u32x2 cvt(f32x4 x) {
+    static __device__ __forceinline__ Xop cvt(f32x4 x) {
         return u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
     }
     static __device__ __forceinline__ u32x2 ld4(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
-    // K = 16: D += A(lds row, 16 cols) * X (acc tile as B, K = its rows)
-    static __device__ __forceinline__ f32x4 lds_acc16(const uint16_t* arow, u32x2 xb, f32x4 acc) {
+    // K = 16: D += A(LDS row) * X (acc tile as B, K = its rows)
+    static __device__ __forceinline__ f32x4 lds_acc16(const uint16_t* arow, Xop xb, f32x4 acc) {
         const int g = (threadIdx.x & 63) >> 4;
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, ld4(arow + 4 * g)),
                                                          __builtin_bit_cast(s16x4, xb), acc, 0, 0, 0);
     }
-    // K = 16: D += X^T (acc tile as A, K = its rows) * B(lds row, 16 cols)
-    static __device__ __forceinline__ f32x4 acc_lds16(u32x2 xa, const uint16_t* brow, f32x4 acc) {
+    // K = 16: D += X^T (acc tile as A, K = its rows) * B(LDS row)
+    static __device__ __forceinline__ f32x4 acc_lds16(Xop xa, const uint16_t* brow, f32x4 acc) {
         const int g = (threadIdx.x & 63) >> 4;
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, xa),
                                                          __builtin_bit_cast(s16x4, ld4(brow + 4 * g)), acc, 0, 0, 0);
     }
-    // K = 32 from two 16-row groups (t1, t2) of the LDS row and two acc tiles.
-    static __device__ __forceinline__ f32x4 lds_acc32(const uint16_t* arow1, const uint16_t* arow2, u32x2 x1, u32x2 x2,
+    // K = 32 from two 16-wide segments of the LDS row and two acc tiles.
+    static __device__ __forceinline__ f32x4 lds_acc32(const uint16_t* arow1, const uint16_t* arow2, Xop x1, Xop x2,
                                                       f32x4 acc) {
         const int g = (threadIdx.x & 63) >> 4;
         const u32x2 a1 = ld4(arow1 + 4 * g), a2 = ld4(arow2 + 4 * g);
@@ -114,11 +118,21 @@ template <> struct Op<uint16_t> {    // bf16 operands
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                        acc, 0, 0, 0);
     }
-    static __device__ __forceinline__ f32x4 acc_lds32(u32x2 x1, u32x2 x2, const uint16_t* brow1, const uint16_t* brow2,
+    static __device__ __forceinline__ f32x4 acc_lds32(Xop x1, Xop x2, const uint16_t* brow1, const uint16_t* brow2,
                                                       f32x4 acc) {
         const int g = (threadIdx.x & 63) >> 4;
         const u32x2 b1 = ld4(brow1 + 4 * g), b2 = ld4(brow2 + 4 * g);
         const u32x4 a = {x1[0], x1[1], x2[0], x2[1]}, b = {b1[0], b1[1], b2[0], b2[1]};
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       acc, 0, 0, 0);
+    }
+    // K = 16 product issued as a K = 32 MFMA with the second half zero, for
+    // accumulators that also receive 16x16x32 products: every MFMA that
+    // accumulates into one register tile then has the same shape.
+    static __device__ __forceinline__ f32x4 acc_lds16_k32(Xop xa, const uint16_t* brow, f32x4 acc) {
+        const int g = (threadIdx.x & 63) >> 4;
+        const u32x2 b1 = ld4(brow + 4 * g);
+        const u32x4 a = {xa[0], xa[1], 0u, 0u}, b = {b1[0], b1[1], 0u, 0u};
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                        acc, 0, 0, 0);
     }
@@ -127,12 +141,12 @@ template <> struct Op<uint16_t> {    // bf16 operands
         *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(x0, x1);
     }
     static __device__ __forceinline__ void put4(uint16_t* p, f32x4 x) { *reinterpret_cast<u32x2*>(p) = cvt(x); }
-    static __device__ __forceinline__ float get(const uint16_t* p) { return bf16_to_f32(*p); }
 };
 
 template <> struct Op<float> {       // fp32 operands
     static constexpr int KS = 4;
     typedef float Frag;
+    typedef f32x4 Xop;
     static __device__ __forceinline__ Frag frag(const float* base, int ld, int k0) {
         const int lane = threadIdx.x & 63;
         return base[(lane & 15) * ld + (lane >> 4) + k0];
@@ -140,42 +154,38 @@ template <> struct Op<float> {       // fp32 operands
     static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
-    static __device__ __forceinline__ f32x4 cvt(f32x4 x) { return x; }
-    static __device__ __forceinline__ f32x4 lds_acc16(const float* arow, f32x4 xb, f32x4 acc) {
+    static __device__ __forceinline__ Xop cvt(f32x4 x) { return x; }
+    static __device__ __forceinline__ f32x4 lds_acc16(const float* arow, Xop xb, f32x4 acc) {
         const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[4 * g + e], xb[e], acc, 0, 0, 0);
         return acc;
     }
-    static __device__ __forceinline__ f32x4 acc_lds16(f32x4 xa, const float* brow, f32x4 acc) {
+    static __device__ __forceinline__ f32x4 acc_lds16(Xop xa, const float* brow, f32x4 acc) {
         const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[e], brow[4 * g + e], acc, 0, 0, 0);
         return acc;
     }
-    static __device__ __forceinline__ f32x4 lds_acc32(const float* arow1, const float* arow2, f32x4 x1, f32x4 x2,
+    static __device__ __forceinline__ f32x4 lds_acc32(const float* arow1, const float* arow2, Xop x1, Xop x2,
                                                       f32x4 acc) {
         return lds_acc16(arow2, x2, lds_acc16(arow1, x1, acc));
     }
-    static __device__ __forceinline__ f32x4 acc_lds32(f32x4 x1, f32x4 x2, const float* brow1, const float* brow2,
+    static __device__ __forceinline__ f32x4 acc_lds32(Xop x1, Xop x2, const float* brow1, const float* brow2,
                                                       f32x4 acc) {
         return acc_lds16(x2, brow2, acc_lds16(x1, brow1, acc));
+    }
+    static __device__ __forceinline__ f32x4 acc_lds16_k32(Xop xa, const float* brow, f32x4 acc) {
+        return acc_lds16(xa, brow, acc);
     }
     static __device__ __forceinline__ void put(float* p, float x) { *p = x; }
     static __device__ __forceinline__ void put2(float* p, float x0, float x1) {
         *reinterpret_cast<f32x2*>(p) = f32x2{x0, x1};
     }
     static __device__ __forceinline__ void put4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
-    static __device__ __forceinline__ float get(const float* p) { return *p; }
 };
 
-// Index of tile-pair block (i, j), j <= i, among the 10 lower blocks.
-__device__ __forceinline__ constexpr int blk(int i, int j) { return i * (i + 1) / 2 + j; }
-
-// ---------------------------------------------------------------------------
-// Raw input words.  q/k words hold CPT packed elements (a bf16 pair, or one
-// bf16 / fp32 element).
-// ---------------------------------------------------------------------------
+// Raw input words: CPT packed elements (a bf16 pair, or one bf16 / fp32 element).
 template <typename T, int CPT>
 __device__ __forceinline__ uint32_t load_word(const T* p) {
     if constexpr (sizeof(T) == 2 && CPT == 2) return *reinterpret_cast<const uint32_t*>(p);
@@ -190,93 +200,78 @@ __device__ __forceinline__ float word_elem(uint32_t w, int cc) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS plan (all buffers live for the whole chunk).
+// LDS plan.  Two buffers (chunk parity) of the state-independent results that
+// the state-dependent half consumes, plus scratch used only inside SI.
 // ---------------------------------------------------------------------------
 template <typename OT, int DK>
 struct Plan {
     static constexpr int ES = sizeof(OT);
-    static constexpr int PAD = (ES == 2) ? 8 : 2;   // row padding (elements)
-    static constexpr int LDK = DK + PAD;            // stride of [*, DK] buffers
-    static constexpr int LDC = kC + PAD;            // stride of [*, C] buffers
-    static constexpr int QE1 = 0;                                  // [C][LDK]  q * e^{g - rho_i}
-    static constexpr int KE1 = QE1 + kC * LDK * ES;                // [C][LDK]  k * e^{g - rho_i}
-    static constexpr int KCOL = KE1 + kC * LDK * ES;               // 10 x [16][LDK] column operands
-    static constexpr int QG = KCOL + 10 * 16 * LDK * ES;           // [C][LDK]  q * e^{g}
-    static constexpr int KG = QG + kC * LDK * ES;                  // [C][LDK]  k * e^{g}
-    static constexpr int KDT = KG + kC * LDK * ES;                 // [DK][LDC] (k * e^{g_C - g})^T
-    static constexpr int PB = KDT + DK * LDC * ES;                 // [C][LDC]  P (lower incl. diagonal)
-    static constexpr int MB = PB + kC * LDC * ES;                  // [C][LDC]  M below the diagonal blocks,
-                                                                   //           A_ii in the diagonal blocks
-    static constexpr int BETA = MB + kC * LDC * ES;                // [C] fp32
-    static constexpr int SX = BETA + kC * 4;                       // [4][DK] fp32 tile log2-decay totals
-    static constexpr int DECAY = SX + kTiles * DK * 4;             // [DK] fp32 e^{g_C}
-    static constexpr int TOTAL = DECAY + DK * 4;
+    static constexpr int PAD = 16 / ES;             // row padding: 16 bytes (keeps 16-byte row alignment)
+    static constexpr int LDK = DK + PAD;            // stride of [*, DK] rows
+    static constexpr int LDC = kC + PAD;            // stride of [*, C] rows
+    static constexpr int LD16 = 16 + PAD;           // stride of 16x16 blocks
+    // one buffer
+    static constexpr int QE1 = 0;                                  // [C][LDK]   q * e1
+    static constexpr int KE1 = QE1 + kC * LDK * ES;                // [C][LDK]   k * e1
+    static constexpr int KE2T = KE1 + kC * LDK * ES;               // [DK][LDC]  (k * e2)^T
+    static constexpr int PD = KE2T + DK * LDC * ES;                // [4][16][LD16] P per tile
+    static constexpr int AD = PD + kTiles * 16 * LD16 * ES;        // [4][16][LD16] A per tile
+    static constexpr int DEC = AD + kTiles * 16 * LD16 * ES;       // [4][DK] fp32 2^X per tile
+    static constexpr int BUF = DEC + kTiles * DK * 4;
+    // scratch
+    static constexpr int KB = 2 * BUF;                             // [C][LDK]   k * 2^{-x}
+    static constexpr int MS = KB + kC * LDK * ES;                  // [4][16][17] fp32 M per tile
+    static constexpr int BS = MS + kTiles * 16 * 17 * 4;           // [4][16] fp32 beta per tile
+    static constexpr int TOTAL = BS + kTiles * 16 * 4;
+    static_assert(BUF % 16 == 0 && KB % 16 == 0, "alignment");
     static_assert(TOTAL <= 160 * 1024, "LDS plan exceeds 160 KB");
 };
 
-// Gram work list: wave w computes the tile pairs (i, j0 .. j0 + cnt - 1) of row tile i,
-// then (i2, j2 .. ) when it has a second row.  Pairs (i, j), j <= i, 10 in total.
-template <int NW> struct GramSched;
-template <> struct GramSched<4> {   // w0: (0,0) (1,0) (1,1)  w1: (2,0..2)  w2: (3,0) (3,1)  w3: (3,2) (3,3)
-    static __device__ __forceinline__ void pair(int w, int p, int& i, int& j, int& cnt) {
-        cnt = w < 2 ? 3 : 2;
-        if (w == 0) { i = p == 0 ? 0 : 1; j = p == 0 ? 0 : p - 1; }
-        else if (w == 1) { i = 2; j = p; }
-        else { i = 3; j = (w == 2 ? 0 : 2) + p; }
-    }
-};
-template <> struct GramSched<8> {   // w0: (0,0)  w1: (1,0) (1,1)  w2: (2,0)  w3: (2,1) (2,2)  w4..w7: (3,0) .. (3,3)
-    static __device__ __forceinline__ void pair(int w, int p, int& i, int& j, int& cnt) {
-        cnt = (w == 1 || w == 3) ? 2 : 1;
-        if (w == 0) { i = 0; j = 0; }
-        else if (w == 1) { i = 1; j = p; }
-        else if (w == 2) { i = 2; j = 0; }
-        else if (w == 3) { i = 2; j = 1 + p; }
-        else { i = 3; j = w - 4; }
-    }
-};
-
-template <typename T, int DK, int DV, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const float* __restrict__ init_state, const int32_t* __restrict__ cu_seqlens,
-    int64_t total_T, int H, T* __restrict__ o, float* __restrict__ final_state) {
+    int64_t total_T, int H, int units, T* __restrict__ o, float* __restrict__ final_state) {
     using OT = T;
     using OP = Op<OT>;
     using PL = Plan<OT, DK>;
+    using Xop = typename OP::Xop;
     constexpr int KS = OP::KS;
-    constexpr int WPT = NW / kTiles;      // phase E: waves per 16-token tile
-    constexpr int CPT = DK / (64 * WPT);  // phase E: channels per thread
+    constexpr int CPT = DK / 64;          // SI: channels per thread
     constexpr int NCT = DK / 16;          // 16-row channel tiles of the state
     constexpr int NKS = DK / KS;          // K-steps of the Gram products
-    constexpr int BV = 16 * NW;           // value columns per workgroup
-    static_assert(CPT == 1 || CPT == 2, "phase E mapping");
-    static_assert(DV % BV == 0, "value blocking");
+    constexpr int NV = DV / kBV;          // value-column workgroups per (sequence, head)
+    static_assert(CPT == 1 || CPT == 2, "SI mapping");
+    static_assert(NV == 1 || NV == 2, "value blocking");
+
+    // Workgroup -> (unit = sequence * H + head, value block).  With two value
+    // blocks, the pair of a unit sits 8 workgroups apart (same XCD).
+    const int lid = blockIdx.x;
+    int unit, vblk;
+    if constexpr (NV == 2) {
+        unit = 8 * (lid >> 4) + (lid & 7);
+        vblk = (lid >> 3) & 1;
+    } else {
+        unit = lid;
+        vblk = 0;
+    }
+    if (unit >= units) return;
+    const int n = unit / H;
+    const int h = unit - n * H;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    OT* sQE1 = reinterpret_cast<OT*>(smem + PL::QE1);
-    OT* sKE1 = reinterpret_cast<OT*>(smem + PL::KE1);
-    OT* sKCOL = reinterpret_cast<OT*>(smem + PL::KCOL);
-    OT* sQG = reinterpret_cast<OT*>(smem + PL::QG);
-    OT* sKG = reinterpret_cast<OT*>(smem + PL::KG);
-    OT* sKDT = reinterpret_cast<OT*>(smem + PL::KDT);
-    OT* sP = reinterpret_cast<OT*>(smem + PL::PB);
-    OT* sM = reinterpret_cast<OT*>(smem + PL::MB);
-    float* sBeta = reinterpret_cast<float*>(smem + PL::BETA);
-    float* sX = reinterpret_cast<float*>(smem + PL::SX);
-    float* sDecay = reinterpret_cast<float*>(smem + PL::DECAY);
+    float* sMS = reinterpret_cast<float*>(smem + PL::MS);
+    float* sBS = reinterpret_cast<float*>(smem + PL::BS);
+    OT* sKB = reinterpret_cast<OT*>(smem + PL::KB);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l16 = lane & 15;
     const int lg = lane >> 4;
-    const int h = blockIdx.y;
-    const int n = blockIdx.z;
-    const int vcol = blockIdx.x * BV + 16 * wave;    // this wave's first value column
-    const int ti = wave / WPT;                        // phase E: tile
-    const int cb = (wave % WPT) * (64 * CPT) + lane * CPT;   // phase E: first channel
+    const int vcol = vblk * kBV + 16 * wave;     // SD: this wave's first value column
+    const int cb = lane * CPT;                   // SI: first key channel of this thread
 
     // Sequence range, clamped so malformed offsets cannot address out of range.
     int64_t seq0 = 0, seq1 = total_T;
@@ -287,6 +282,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(
         seq1 = seq1 < seq0 ? seq0 : (seq1 > total_T ? total_T : seq1);
     }
     const int64_t len = seq1 - seq0;
+    const int64_t nchunks = (len + kC - 1) / kC;
 
     // This wave's state slab: Sacc[ct][e] = S[16 ct + 4 lg + e][vcol + l16].
     f32x4 Sacc[NCT];
@@ -297,18 +293,19 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(
         for (int e = 0; e < 4; ++e)
             Sacc[ct][e] = init_state ? init_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] : 0.f;
 
-    // Raw-input prefetch registers.  Positions past the chunk's end are
-    // clamped to its last token (always a valid address) and zeroed when used.
+    // ---- prefetch registers (one chunk ahead).  Positions past a chunk's end
+    // are clamped to its last token (a valid address) and zeroed when used.
     float la_r[16][CPT];
     uint32_t qw_r[16], kw_r[16];
     float beta_r;
-    uint32_t v_r[kTiles][4];   // v[16 i + 4 lg + e][vcol + l16]
-    auto load_e = [&](int64_t c0n) {
-        const int Ln = (int)((len - c0n) < kC ? (len - c0n) : kC);
+    uint32_t v_r[kTiles][4];     // v[16 i + 4 lg + e][vcol + l16]
+    auto chunk_len = [&](int64_t c) { return (int)((len - c * kC) < kC ? (len - c * kC) : kC); };
+    auto load_si = [&](int64_t c) {
+        const int Ln = chunk_len(c);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int pos = 16 * ti + r < Ln ? 16 * ti + r : Ln - 1;
-            const int64_t row = (seq0 + c0n + pos) * H + h;
+            const int p = 16 * wave + r;
+            const int64_t row = (seq0 + c * kC + (p < Ln ? p : Ln - 1)) * H + h;
             if constexpr (CPT == 2) {
                 const f32x2 la2 = *reinterpret_cast<const f32x2*>(log_alpha + row * DK + cb);
                 la_r[r][0] = la2[0];
@@ -319,248 +316,208 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(
             qw_r[r] = load_word<T, CPT>(q + row * DK + cb);
             kw_r[r] = load_word<T, CPT>(k + row * DK + cb);
         }
-        const int bp = tid < Ln ? tid : Ln - 1;
-        beta_r = tid < kC ? beta[(seq0 + c0n + bp) * H + h] : 0.f;
+        const int p = 16 * wave + l16;
+        beta_r = beta[(seq0 + c * kC + (p < Ln ? p : Ln - 1)) * H + h];
     };
-    auto load_v = [&](int64_t c0n) {
-        const int Ln = (int)((len - c0n) < kC ? (len - c0n) : kC);
+    auto load_v = [&](int64_t c) {
+        const int Ln = chunk_len(c);
 #pragma unroll
         for (int i = 0; i < kTiles; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int p = 16 * i + 4 * lg + e;
-                const int pos = p < Ln ? p : Ln - 1;
-                v_r[i][e] = load_word<T, 1>(v + ((seq0 + c0n + pos) * H + h) * DV + vcol + l16);
+                v_r[i][e] = load_word<T, 1>(v + ((seq0 + c * kC + (p < Ln ? p : Ln - 1)) * H + h) * DV + vcol + l16);
             }
     };
-    if (len > 0) {
-        load_e(0);
-        load_v(0);
-    }
 
-    for (int64_t c0 = 0; c0 < len; c0 += kC) {
-        const int L = (int)((len - c0) < kC ? (len - c0) : kC);
-        const int64_t tok0 = seq0 + c0;
-        const bool has_next = c0 + kC < len;
-
-        // ---------------- phase E: decay factors and scaled operands ----------------
-        {
-            float al[16][CPT], xs[CPT];
+    // ---- SI: state-independent results of chunk c into buffer (c & 1).  Wave i = tile i.
+    auto si = [&](int64_t c) {
+        unsigned char* buf = smem + (c & 1) * PL::BUF;
+        OT* sQE1 = reinterpret_cast<OT*>(buf + PL::QE1);
+        OT* sKE1 = reinterpret_cast<OT*>(buf + PL::KE1);
+        OT* sKE2T = reinterpret_cast<OT*>(buf + PL::KE2T);
+        OT* sPD = reinterpret_cast<OT*>(buf + PL::PD);
+        OT* sAD = reinterpret_cast<OT*>(buf + PL::AD);
+        float* sDEC = reinterpret_cast<float*>(buf + PL::DEC);
+        const int Lc = chunk_len(c);
+        const int ti = wave;
+        // decay factors: alpha = 2^{l2}; e1 = prefix products, e2 = suffix products (excluding r)
+        float al[16][CPT], xs[CPT];
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) xs[cc] = 0.f;
+        for (int cc = 0; cc < CPT; ++cc) xs[cc] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool ok = 16 * ti + r < L;
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    const float l2 = ok ? la_r[r][cc] * kLog2e : 0.f;
-                    xs[cc] += l2;
-                    al[r][cc] = fexp2(l2);
-                }
-            }
-            if (tid < kC) sBeta[tid] = tid < L ? beta_r : 0.f;
-#pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) sX[ti * DK + cb + cc] = xs[cc];
-            // e1[r] = prod_{s<=r} alpha_s (relative to the tile start),
-            // e2[r] = prod_{s>r} alpha_s  (remaining decay to the tile end).
-            float e1[16][CPT], e2[16][CPT];
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
-                float p = 1.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) { p *= al[r][cc]; e1[r][cc] = p; }
-                p = 1.f;
-#pragma unroll
-                for (int r = 15; r >= 0; --r) { e2[r][cc] = p; p *= al[r][cc]; }
+                const float l2 = (16 * ti + r < Lc) ? la_r[r][cc] * kLog2e : 0.f;
+                xs[cc] += l2;
+                al[r][cc] = fexp2(l2);
             }
-            __syncthreads();
-
-            // Per-channel factors from the tiles' log2-decay totals.
-            float fG[CPT], fD[CPT], F[kTiles][CPT];
+        float e2[16][CPT], fB[CPT];
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+            float p = 1.f;
+#pragma unroll
+            for (int r = 15; r >= 0; --r) { e2[r][cc] = p; p *= al[r][cc]; }
+            fB[cc] = fexp2(-xs[cc]);
+            sDEC[ti * DK + cb + cc] = fexp2(xs[cc]);
+        }
+        float e1[CPT];
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) e1[cc] = 1.f;
+        float ke2[CPT][16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int pos = 16 * ti + r;
+            const bool ok = pos < Lc;
+            float qe1[CPT], ke1[CPT], kb[CPT];
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) {
-                float rho[kTiles + 1];
-                rho[0] = 0.f;
-#pragma unroll
-                for (int j = 0; j < kTiles; ++j) rho[j + 1] = rho[j] + sX[j * DK + cb + cc];
-                if (ti == 0) sDecay[cb + cc] = fexp2(rho[kTiles]);
-                fG[cc] = fexp2(rho[ti]);                               // e^{rho_i}
-                fD[cc] = fexp2(rho[kTiles] - rho[ti + 1]);             // e^{g_C - rho_{i+1}}
-#pragma unroll
-                for (int ip = 0; ip < kTiles; ++ip)                    // column factor for row tile ip
-                    F[ip][cc] = (ip == ti) ? fexp2(-xs[cc]) : (ip > ti + 1 ? fexp2(rho[ip] - rho[ti + 1]) : 1.f);
+                e1[cc] *= al[r][cc];
+                const float qv = ok ? word_elem<T>(qw_r[r], cc) : 0.f;
+                const float kv = ok ? word_elem<T>(kw_r[r], cc) : 0.f;
+                qe1[cc] = qv * e1[cc];
+                ke1[cc] = kv * e1[cc];
+                ke2[cc][r] = kv * e2[r][cc];
+                kb[cc] = ke2[cc][r] * fB[cc];
             }
-            float kd[CPT][16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int pos = 16 * ti + r;
-                const bool ok = pos < L;
-                float qe1[CPT], ke1[CPT], ke2[CPT];
-#pragma unroll
-                for (int cc = 0; cc < CPT; ++cc) {
-                    const float qv = ok ? word_elem<T>(qw_r[r], cc) : 0.f;
-                    const float kv = ok ? word_elem<T>(kw_r[r], cc) : 0.f;
-                    qe1[cc] = qv * e1[r][cc];
-                    ke1[cc] = kv * e1[r][cc];
-                    ke2[cc] = kv * e2[r][cc];
-                    kd[cc][r] = ke2[cc] * fD[cc];
-                }
-                const int o_row = pos * PL::LDK + cb;
-                if constexpr (CPT == 2) {
-                    OP::put2(sQE1 + o_row, qe1[0], qe1[CPT - 1]);
-                    OP::put2(sKE1 + o_row, ke1[0], ke1[CPT - 1]);
-                    OP::put2(sQG + o_row, qe1[0] * fG[0], qe1[CPT - 1] * fG[CPT - 1]);
-                    OP::put2(sKG + o_row, ke1[0] * fG[0], ke1[CPT - 1] * fG[CPT - 1]);
-#pragma unroll
-                    for (int ip = 0; ip < kTiles; ++ip)
-                        if (ip >= ti)
-                            OP::put2(sKCOL + (blk(ip, ti) * 16 + r) * PL::LDK + cb, ke2[0] * F[ip][0],
-                                     ke2[CPT - 1] * F[ip][CPT - 1]);
-                } else {
-                    OP::put(sQE1 + o_row, qe1[0]);
-                    OP::put(sKE1 + o_row, ke1[0]);
-                    OP::put(sQG + o_row, qe1[0] * fG[0]);
-                    OP::put(sKG + o_row, ke1[0] * fG[0]);
-#pragma unroll
-                    for (int ip = 0; ip < kTiles; ++ip)
-                        if (ip >= ti) OP::put(sKCOL + (blk(ip, ti) * 16 + r) * PL::LDK + cb, ke2[0] * F[ip][0]);
-                }
+            const int orow = pos * PL::LDK + cb;
+            if constexpr (CPT == 2) {
+                OP::put2(sQE1 + orow, qe1[0], qe1[CPT - 1]);
+                OP::put2(sKE1 + orow, ke1[0], ke1[CPT - 1]);
+                OP::put2(sKB + orow, kb[0], kb[CPT - 1]);
+            } else {
+                OP::put(sQE1 + orow, qe1[0]);
+                OP::put(sKE1 + orow, ke1[0]);
+                OP::put(sKB + orow, kb[0]);
             }
-#pragma unroll
-            for (int cc = 0; cc < CPT; ++cc)
-#pragma unroll
-                for (int r = 0; r < 16; r += 4) {
-                    f32x4 w4 = {kd[cc][r], kd[cc][r + 1], kd[cc][r + 2], kd[cc][r + 3]};
-                    OP::put4(sKDT + (cb + cc) * PL::LDC + 16 * ti + r, w4);
-                }
         }
-        if (has_next) load_e(c0 + kC);      // prefetch: in flight during phases G..SD
-        __syncthreads();
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc)
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+                const f32x4 w4 = {ke2[cc][r], ke2[cc][r + 1], ke2[cc][r + 2], ke2[cc][r + 3]};
+                OP::put4(sKE2T + (cb + cc) * PL::LDC + 16 * ti + r, w4);
+            }
+        if (lane < 16) sBS[ti * 16 + lane] = (16 * ti + lane < Lc) ? beta_r : 0.f;
+        wave_lds_sync();
 
-        // ---------------- phase G: P and M tile products ----------------
-        // Both computed transposed (D[s][r] = sum_c Kcol[s][c] X[r][c]) so that
-        // each lane holds 4 consecutive columns s of one row r, stored row-major.
+        // P and M of the tile, transposed (D[s][r] = sum_c Kb[s][c] X[r][c]):
+        // lane holds row r = l16, columns s = 4 lg + e.
         {
-            int ci, cj, cnt;
-            GramSched<NW>::pair(wave, 0, ci, cj, cnt);
-            typename OP::Frag fq[NKS], fk[NKS];
-            int loaded_i = -1;
-            for (int p = 0; p < cnt; ++p) {
-                GramSched<NW>::pair(wave, p, ci, cj, cnt);
-                if (ci != loaded_i) {
+            const OT* rq = sQE1 + 16 * ti * PL::LDK;
+            const OT* rk = sKE1 + 16 * ti * PL::LDK;
+            const OT* rb = sKB + 16 * ti * PL::LDK;
+            f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        fq[ks] = OP::frag(sQE1 + 16 * ci * PL::LDK, PL::LDK, ks * KS);
-                        fk[ks] = OP::frag(sKE1 + 16 * ci * PL::LDK, PL::LDK, ks * KS);
-                    }
-                    loaded_i = ci;
-                }
-                const OT* colb = sKCOL + blk(ci, cj) * 16 * PL::LDK;
-                f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const typename OP::Frag fc = OP::frag(colb, PL::LDK, ks * KS);
-                    accP = OP::mma(fc, fq[ks], accP);
-                    accM = OP::mma(fc, fk[ks], accM);
-                }
-                // row r = l16 of tile ci, columns s = 4 lg + e of tile cj
-                f32x4 vp, vm;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vp[e] = (ci > cj || 4 * lg + e <= l16) ? accP[e] : 0.f;
-                    vm[e] = (ci > cj || 4 * lg + e < l16) ? accM[e] : 0.f;
-                }
-                OP::put4(sP + (16 * ci + l16) * PL::LDC + 16 * cj + 4 * lg, vp);
-                OP::put4(sM + (16 * ci + l16) * PL::LDC + 16 * cj + 4 * lg, vm);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const typename OP::Frag fb = OP::frag(rb, PL::LDK, ks * KS);
+                accP = OP::mma(fb, OP::frag(rq, PL::LDK, ks * KS), accP);
+                accM = OP::mma(fb, OP::frag(rk, PL::LDK, ks * KS), accM);
             }
+            f32x4 vp;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 4 * lg + e;
+                vp[e] = s <= l16 ? accP[e] : 0.f;
+                sMS[(ti * 16 + l16) * 17 + s] = s < l16 ? accM[e] : 0.f;
+            }
+            OP::put4(sPD + (ti * 16 + l16) * PL::LD16 + 4 * lg, vp);
         }
-        __syncthreads();
+        wave_lds_sync();
 
-        // ---------------- phase S: diagonal blocks A_ii = (I + Diag(b_i) M_ii)^{-1} Diag(b_i) ----------------
-        // Wave i < 4 inverts block i, lane j < 16 owns column j of T_ii:
-        //   t_r = [r == j] - b_r sum_{s<r} M_rs t_s   (right-looking), A_ii[r][j] = t_r b_j.
-        if (wave < kTiles && lane < 16) {
-            const int base = 16 * wave;
+        // A = (I + Diag(b) M)^{-1} Diag(b): lane j < 16 owns column j of the
+        // inverse, right-looking substitution t_r = [r == j] - b_r sum_{s<r} M_rs t_s.
+        if (lane < 16) {
+            const float* Mt = sMS + ti * 16 * 17;
+            const float* bt = sBS + ti * 16;
             const int j = lane;
             float acc[16], t[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
-                t[s] = (s == j ? 1.f : 0.f) - sBeta[base + s] * acc[s];
+                t[s] = (s == j ? 1.f : 0.f) - bt[s] * acc[s];
 #pragma unroll
-                for (int r = s + 1; r < 16; ++r) acc[r] += OP::get(sM + (base + r) * PL::LDC + base + s) * t[s];
+                for (int r = s + 1; r < 16; ++r) acc[r] += Mt[r * 17 + s] * t[s];
             }
-            const float bj = sBeta[base + j];
+            const float bj = bt[j];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) OP::put(sM + (base + r) * PL::LDC + base + j, t[r] * bj);
+            for (int r = 0; r < 16; ++r) OP::put(sAD + (ti * 16 + r) * PL::LD16 + j, t[r] * bj);
         }
-        __syncthreads();
+    };
 
-        // ---------------- phase SD: state-dependent part, wave-local ----------------
-        {
-            typedef decltype(OP::cvt(Sacc[0])) Xop;
+    // ---- SD: state-dependent part of chunk c from buffer (c & 1).  Wave w = value columns.
+    auto sd = [&](int64_t c) {
+        const unsigned char* buf = smem + (c & 1) * PL::BUF;
+        const OT* sQE1 = reinterpret_cast<const OT*>(buf + PL::QE1);
+        const OT* sKE1 = reinterpret_cast<const OT*>(buf + PL::KE1);
+        const OT* sKE2T = reinterpret_cast<const OT*>(buf + PL::KE2T);
+        const OT* sPD = reinterpret_cast<const OT*>(buf + PL::PD);
+        const OT* sAD = reinterpret_cast<const OT*>(buf + PL::AD);
+        const float* sDEC = reinterpret_cast<const float*>(buf + PL::DEC);
+        const int Lc = chunk_len(c);
+        const int64_t tok0 = seq0 + c * kC;
+#pragma unroll
+        for (int i = 0; i < kTiles; ++i) {
             Xop Sop[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) Sop[ct] = OP::cvt(Sacc[ct]);
-
-            // U_i = V_i - K_Gamma,i S0;  W_i = A_ii (U_i - sum_{j<i} M_ij W_j).
-            // Tiles hold D[r][v]: lane (v = l16, r = 16 i + 4 lg + e).
-            Xop Wop[kTiles];
+            // U = V_i - (K e1)_i S   (D[r][v]: lane v = l16, rows r = 4 lg + e)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const OT* krow = sKE1 + (16 * i + l16) * PL::LDK;
 #pragma unroll
-            for (int i = 0; i < kTiles; ++i) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const OT* kgrow = sKG + (16 * i + l16) * PL::LDK;
+            for (int ct = 0; ct < NCT; ct += 2)
+                acc = OP::lds_acc32(krow + 16 * ct, krow + 16 * (ct + 1), Sop[ct], Sop[ct + 1], acc);
+            f32x4 y;
 #pragma unroll
-                for (int ct = 0; ct < NCT; ct += 2)
-                    acc = OP::lds_acc32(kgrow + 16 * ct, kgrow + 16 * (ct + 1), Sop[ct], Sop[ct + 1], acc);
-                const OT* mrow = sM + (16 * i + l16) * PL::LDC;
-#pragma unroll
-                for (int j = 0; j < i; ++j) acc = OP::lds_acc16(mrow + 16 * j, Wop[j], acc);
-                f32x4 y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float vv = (16 * i + 4 * lg + e < L) ? word_elem<T>(v_r[i][e], 0) : 0.f;
-                    y[e] = vv - acc[e];
-                }
-                f32x4 w = {0.f, 0.f, 0.f, 0.f};
-                w = OP::lds_acc16(mrow + 16 * i, OP::cvt(y), w);
-                Wop[i] = OP::cvt(w);
+            for (int e = 0; e < 4; ++e) {
+                const float vv = (16 * i + 4 * lg + e < Lc) ? word_elem<T>(v_r[i][e], 0) : 0.f;
+                y[e] = vv - acc[e];
             }
-            if (has_next) load_v(c0 + kC);
-
-            // O_i^T = S0^T Q_Gamma,i^T + sum_{j<=i} W_j^T P_ij^T: lane (r = l16, v = 4 lg + e).
+            // W = A U
+            f32x4 w = {0.f, 0.f, 0.f, 0.f};
+            w = OP::lds_acc16(sAD + (16 * i + l16) * PL::LD16, OP::cvt(y), w);
+            const Xop Wop = OP::cvt(w);
+            // O^T = S^T (Q e1)^T + W^T P^T   (lane: row r = l16, columns 4 lg + e)
+            f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+            const OT* qrow = sQE1 + (16 * i + l16) * PL::LDK;
 #pragma unroll
-            for (int i = 0; i < kTiles; ++i) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const OT* qgrow = sQG + (16 * i + l16) * PL::LDK;
-#pragma unroll
-                for (int ct = 0; ct < NCT; ct += 2)
-                    acc = OP::acc_lds32(Sop[ct], Sop[ct + 1], qgrow + 16 * ct, qgrow + 16 * (ct + 1), acc);
-                const OT* prow = sP + (16 * i + l16) * PL::LDC;
-#pragma unroll
-                for (int j = 0; j <= i; ++j) acc = OP::acc_lds16(Wop[j], prow + 16 * j, acc);
-                const int pos = 16 * i + l16;
-                if (pos < L) {
-                    T* dst = o + ((tok0 + pos) * H + h) * DV + vcol + 4 * lg;
-                    if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x2*>(dst) = OP::cvt(acc);
-                    else *reinterpret_cast<f32x4*>(dst) = acc;
-                }
+            for (int ct = 0; ct < NCT; ct += 2)
+                oacc = OP::acc_lds32(Sop[ct], Sop[ct + 1], qrow + 16 * ct, qrow + 16 * (ct + 1), oacc);
+            oacc = OP::acc_lds16_k32(Wop, sPD + (16 * i + l16) * PL::LD16, oacc);
+            const int pos = 16 * i + l16;
+            if (pos < Lc) {
+                T* dst = o + ((tok0 + pos) * H + h) * DV + vcol + 4 * lg;
+                if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x2*>(dst) = OP::cvt(oacc);
+                else *reinterpret_cast<f32x4*>(dst) = oacc;
             }
-
-            // S <- Diag(Gamma_C) S0 + Kd^T W: lane (v = l16, c = 16 ct + 4 lg + e).
+            // S <- Diag(2^X) S + (K e2)^T W   (lane v = l16, rows c = 16 ct + 4 lg + e)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 acc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = Sacc[ct][e] * sDecay[16 * ct + 4 * lg + e];
-                const OT* kdrow = sKDT + (16 * ct + l16) * PL::LDC;
-                acc = OP::lds_acc32(kdrow, kdrow + 16, Wop[0], Wop[1], acc);
-                acc = OP::lds_acc32(kdrow + 32, kdrow + 48, Wop[2], Wop[3], acc);
-                Sacc[ct] = acc;
+                const f32x4 dec = *reinterpret_cast<const f32x4*>(sDEC + i * DK + 16 * ct + 4 * lg);
+                f32x4 a = Sacc[ct] * dec;
+                a = OP::lds_acc16(sKE2T + (16 * ct + l16) * PL::LDC + 16 * i, Wop, a);
+                Sacc[ct] = a;
             }
         }
+    };
+
+    if (nchunks > 0) {
+        load_si(0);
+        load_v(0);
+        si(0);
+        if (nchunks > 1) load_si(1);
         __syncthreads();
+        for (int64_t c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) {
+                si(c + 1);
+                if (c + 2 < nchunks) load_si(c + 2);
+            }
+            sd(c);
+            if (c + 1 < nchunks) load_v(c + 1);
+            __syncthreads();
+        }
     }
 
     if (final_state != nullptr) {
@@ -572,10 +529,10 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(
     }
 }
 
-template <typename T, int DK, int DV, int NW>
+template <typename T, int DK, int DV>
 hipError_t launch_t(const PrefillArgs& a) {
     using PL = Plan<T, DK>;
-    auto kern = prefill_kernel<T, DK, DV, NW>;
+    auto kern = prefill_kernel<T, DK, DV>;
     static bool attr_set = false;   // per instantiation; the attribute is a property of the function
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -583,10 +540,12 @@ hipError_t launch_t(const PrefillArgs& a) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    dim3 grid(DV / (16 * NW), a.H, a.N);
-    hipLaunchKernelGGL(kern, grid, dim3(64 * NW), PL::TOTAL, a.stream,
+    const int64_t units = (int64_t)a.N * a.H;
+    constexpr int NV = DV / kBV;
+    const int64_t blocks = NV == 2 ? 16 * ((units + 7) / 8) : units;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kNW), PL::TOTAL, a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.init_state,
-                       a.cu_seqlens, a.total_T, a.H, (T*)a.o, a.final_state);
+                       a.cu_seqlens, a.total_T, a.H, (int)units, (T*)a.o, a.final_state);
     return hipGetLastError();
 }
 
@@ -594,11 +553,11 @@ hipError_t launch_t(const PrefillArgs& a) {
 
 hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.bf16) {
-        if (a.d_k == 128) return a.d_v == 128 ? launch_t<uint16_t, 128, 128, 4>(a) : launch_t<uint16_t, 128, 64, 4>(a);
-        return a.d_v == 128 ? launch_t<uint16_t, 64, 128, 4>(a) : launch_t<uint16_t, 64, 64, 4>(a);
+        if (a.d_k == 128) return a.d_v == 128 ? launch_t<uint16_t, 128, 128>(a) : launch_t<uint16_t, 128, 64>(a);
+        return a.d_v == 128 ? launch_t<uint16_t, 64, 128>(a) : launch_t<uint16_t, 64, 64>(a);
     }
     // fp32 operands: d_k = 64 only (the LDS plan of d_k = 128 would exceed 160 KB).
-    return a.d_v == 128 ? launch_t<float, 64, 128, 4>(a) : launch_t<float, 64, 64, 4>(a);
+    return a.d_v == 128 ? launch_t<float, 64, 128>(a) : launch_t<float, 64, 64>(a);
 }
 
 }  // namespace kda
