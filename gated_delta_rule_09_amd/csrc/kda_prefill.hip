@@ -59,8 +59,10 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kC = 64;        // chunk length (tokens per pipeline step)
 constexpr int kTiles = 4;     // 16-token tiles per chunk
-constexpr int kNW = 4;        // waves per workgroup
-constexpr int kBV = 16 * kNW; // value columns per workgroup
+constexpr int kSIW = 4;       // state-independent waves (one per 16-token tile)
+constexpr int kSDW = 4;       // state-dependent waves (16 value columns each)
+constexpr int kNW = kSIW + kSDW;
+constexpr int kBV = 16 * kSDW; // value columns per workgroup
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -126,6 +128,31 @@ template <> struct Op<uint16_t> {    // bf16 operands
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                        acc, 0, 0, 0);
     }
+    // Segments: the 4 consecutive K elements of an LDS row that lane group g
+    // supplies (row + 4g), loaded ahead of the MFMA that consumes them.
+    typedef u32x2 Seg;
+    static __device__ __forceinline__ Seg seg(const uint16_t* row) {
+        return ld4(row + 4 * ((threadIdx.x & 63) >> 4));
+    }
+    static __device__ __forceinline__ f32x4 seg_acc16(Seg a, Xop xb, f32x4 acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, xb),
+                                                         acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 seg_acc32(Seg a1, Seg a2, Xop x1, Xop x2, f32x4 acc) {
+        const u32x4 a = {a1[0], a1[1], a2[0], a2[1]}, b = {x1[0], x1[1], x2[0], x2[1]};
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 acc_seg32(Xop x1, Xop x2, Seg b1, Seg b2, f32x4 acc) {
+        const u32x4 a = {x1[0], x1[1], x2[0], x2[1]}, b = {b1[0], b1[1], b2[0], b2[1]};
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 acc_seg16_k32(Xop xa, Seg b1, f32x4 acc) {
+        const u32x4 a = {xa[0], xa[1], 0u, 0u}, b = {b1[0], b1[1], 0u, 0u};
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       acc, 0, 0, 0);
+    }
     // K = 16 product issued as a K = 32 MFMA with the second half zero, for
     // accumulators that also receive 16x16x32 products: every MFMA that
     // accumulates into one register tile then has the same shape.
@@ -178,6 +205,27 @@ template <> struct Op<float> {       // fp32 operands
     static __device__ __forceinline__ f32x4 acc_lds16_k32(Xop xa, const float* brow, f32x4 acc) {
         return acc_lds16(xa, brow, acc);
     }
+    typedef f32x4 Seg;
+    static __device__ __forceinline__ Seg seg(const float* row) {
+        return *reinterpret_cast<const f32x4*>(row + 4 * ((threadIdx.x & 63) >> 4));
+    }
+    static __device__ __forceinline__ f32x4 seg_acc16(Seg a, Xop xb, f32x4 acc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], xb[e], acc, 0, 0, 0);
+        return acc;
+    }
+    static __device__ __forceinline__ f32x4 acc_seg16(Xop xa, Seg b, f32x4 acc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[e], b[e], acc, 0, 0, 0);
+        return acc;
+    }
+    static __device__ __forceinline__ f32x4 seg_acc32(Seg a1, Seg a2, Xop x1, Xop x2, f32x4 acc) {
+        return seg_acc16(a2, x2, seg_acc16(a1, x1, acc));
+    }
+    static __device__ __forceinline__ f32x4 acc_seg32(Xop x1, Xop x2, Seg b1, Seg b2, f32x4 acc) {
+        return acc_seg16(x2, b2, acc_seg16(x1, b1, acc));
+    }
+    static __device__ __forceinline__ f32x4 acc_seg16_k32(Xop xa, Seg b, f32x4 acc) { return acc_seg16(xa, b, acc); }
     static __device__ __forceinline__ void put(float* p, float x) { *p = x; }
     static __device__ __forceinline__ void put2(float* p, float x0, float x1) {
         *reinterpret_cast<f32x2*>(p) = f32x2{x0, x1};
@@ -197,6 +245,13 @@ template <typename T>
 __device__ __forceinline__ float word_elem(uint32_t w, int cc) {
     if constexpr (sizeof(T) == 2) return cc == 0 ? bf16_lo(w) : bf16_hi(w);
     else return __uint_as_float(w);
+}
+
+// Element cc of a lane's packed words (bf16: two per word; fp32: one per word).
+template <typename T, int N>
+__device__ __forceinline__ float lane_elem(const uint32_t (&w)[N], int cc) {
+    if constexpr (sizeof(T) == 2) return word_elem<T>(w[cc / 2], cc % 2);
+    else return __uint_as_float(w[cc]);
 }
 
 // ---------------------------------------------------------------------------
@@ -220,8 +275,9 @@ struct Plan {
     static constexpr int BUF = DEC + kTiles * DK * 4;
     // scratch
     static constexpr int KB = 2 * BUF;                             // [C][LDK]   k * 2^{-x}
-    static constexpr int MS = KB + kC * LDK * ES;                  // [4][16][17] fp32 M per tile
-    static constexpr int BS = MS + kTiles * 16 * 17 * 4;           // [4][16] fp32 beta per tile
+    static constexpr int MSTR = 20;                                // fp32 stride of M^T rows (16-byte aligned)
+    static constexpr int MS = KB + kC * LDK * ES;                  // [4][16][MSTR] fp32 M^T per tile
+    static constexpr int BS = MS + kTiles * 16 * MSTR * 4;         // [4][16] fp32 beta per tile
     static constexpr int TOTAL = BS + kTiles * 16 * 4;
     static_assert(BUF % 16 == 0 && KB % 16 == 0, "alignment");
     static_assert(TOTAL <= 160 * 1024, "LDS plan exceeds 160 KB");
@@ -238,11 +294,12 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     using PL = Plan<OT, DK>;
     using Xop = typename OP::Xop;
     constexpr int KS = OP::KS;
-    constexpr int CPT = DK / 64;          // SI: channels per thread
+    constexpr int CPL = DK / 32;          // SI: key channels per lane (lane = channel group x half tile)
+    constexpr int QWN = CPL * (int)sizeof(T) / 4;   // 32-bit words holding CPL q (or k) elements
     constexpr int NCT = DK / 16;          // 16-row channel tiles of the state
     constexpr int NKS = DK / KS;          // K-steps of the Gram products
     constexpr int NV = DV / kBV;          // value-column workgroups per (sequence, head)
-    static_assert(CPT == 1 || CPT == 2, "SI mapping");
+    static_assert(CPL == 2 || CPL == 4, "SI mapping");
     static_assert(NV == 1 || NV == 2, "value blocking");
 
     // Workgroup -> (unit = sequence * H + head, value block).  With two value
@@ -270,8 +327,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     const int lane = tid & 63;
     const int l16 = lane & 15;
     const int lg = lane >> 4;
-    const int vcol = vblk * kBV + 16 * wave;     // SD: this wave's first value column
-    const int cb = lane * CPT;                   // SI: first key channel of this thread
+    const int vcol = vblk * kBV + 16 * (wave - kSIW);   // SD waves: first value column
+    const int cb = (lane & 31) * CPL;            // SI: first key channel of this lane
+    const int half = lane >> 5;                  // SI: which 8 positions of the tile
 
     // Sequence range, clamped so malformed offsets cannot address out of range.
     int64_t seq0 = 0, seq1 = total_T;
@@ -284,49 +342,57 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     const int64_t len = seq1 - seq0;
     const int64_t nchunks = (len + kC - 1) / kC;
 
-    // This wave's state slab: Sacc[ct][e] = S[16 ct + 4 lg + e][vcol + l16].
-    f32x4 Sacc[NCT];
-    const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            Sacc[ct][e] = init_state ? init_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] : 0.f;
-
     // ---- prefetch registers (one chunk ahead).  Positions past a chunk's end
     // are clamped to its last token (a valid address) and zeroed when used.
-    float la_r[16][CPT];
-    uint32_t qw_r[16], kw_r[16];
+    float la_r[8][CPL];
+    uint32_t qw_r[8][QWN], kw_r[8][QWN];
     float beta_r;
     uint32_t v_r[kTiles][4];     // v[16 i + 4 lg + e][vcol + l16]
     auto chunk_len = [&](int64_t c) { return (int)((len - c * kC) < kC ? (len - c * kC) : kC); };
+    // One 64-bit base per chunk, then 32-bit offsets; rows past the chunk's
+    // end are clamped to its last token.
     auto load_si = [&](int64_t c) {
-        const int Ln = chunk_len(c);
+        const int pmax = chunk_len(c) - 1 - 16 * wave - 8 * half;   // last valid row of this lane's 8 (may be < 0)
+        const int64_t row0 = (seq0 + c * kC + 16 * wave + 8 * half) * H + h;
+        const float* la0 = log_alpha + row0 * DK + cb;
+        const T* q0 = q + row0 * DK + cb;
+        const T* k0 = k + row0 * DK + cb;
+        const int stride = H * DK;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int p = 16 * wave + r;
-            const int64_t row = (seq0 + c * kC + (p < Ln ? p : Ln - 1)) * H + h;
-            if constexpr (CPT == 2) {
-                const f32x2 la2 = *reinterpret_cast<const f32x2*>(log_alpha + row * DK + cb);
-                la_r[r][0] = la2[0];
-                la_r[r][CPT - 1] = la2[1];
+        for (int r = 0; r < 8; ++r) {
+            const int off = (r < pmax ? r : pmax) * stride;
+            if constexpr (CPL == 4) {
+                const f32x4 la4 = *reinterpret_cast<const f32x4*>(la0 + off);
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) la_r[r][cc] = la4[cc];
             } else {
-                la_r[r][0] = log_alpha[row * DK + cb];
+                const f32x2 la2 = *reinterpret_cast<const f32x2*>(la0 + off);
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) la_r[r][cc] = la2[cc];
             }
-            qw_r[r] = load_word<T, CPT>(q + row * DK + cb);
-            kw_r[r] = load_word<T, CPT>(k + row * DK + cb);
+            if constexpr (QWN == 2) {
+                const u32x2 qv = *reinterpret_cast<const u32x2*>(q0 + off);
+                const u32x2 kv = *reinterpret_cast<const u32x2*>(k0 + off);
+                qw_r[r][0] = qv[0]; qw_r[r][QWN - 1] = qv[1];
+                kw_r[r][0] = kv[0]; kw_r[r][QWN - 1] = kv[1];
+            } else {
+                qw_r[r][0] = *reinterpret_cast<const uint32_t*>(q0 + off);
+                kw_r[r][0] = *reinterpret_cast<const uint32_t*>(k0 + off);
+            }
         }
-        const int p = 16 * wave + l16;
-        beta_r = beta[(seq0 + c * kC + (p < Ln ? p : Ln - 1)) * H + h];
+        const int pb = chunk_len(c) - 1 - 16 * wave;
+        beta_r = beta[(seq0 + c * kC + 16 * wave) * H + h + (l16 < pb ? l16 : pb) * H];
     };
     auto load_v = [&](int64_t c) {
-        const int Ln = chunk_len(c);
+        const int pmax = chunk_len(c) - 1;
+        const T* v0 = v + ((seq0 + c * kC) * H + h) * DV + vcol + l16;
+        const int stride = H * DV;
 #pragma unroll
         for (int i = 0; i < kTiles; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int p = 16 * i + 4 * lg + e;
-                v_r[i][e] = load_word<T, 1>(v + ((seq0 + c * kC + (p < Ln ? p : Ln - 1)) * H + h) * DV + vcol + l16);
+                v_r[i][e] = load_word<T, 1>(v0 + (p < pmax ? p : pmax) * stride);
             }
     };
 
@@ -341,63 +407,72 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         float* sDEC = reinterpret_cast<float*>(buf + PL::DEC);
         const int Lc = chunk_len(c);
         const int ti = wave;
-        // decay factors: alpha = 2^{l2}; e1 = prefix products, e2 = suffix products (excluding r)
-        float al[16][CPT], xs[CPT];
+        // Lane = (channel group cb .. cb+CPL-1, positions pb .. pb+7 of the tile).
+        // alpha = 2^{l2}; e1 = prefix products over the tile, e2 = suffix
+        // products excluding r.  Each half forms its own running products; the
+        // halves then exchange their totals.
+        const int pb = 16 * ti + 8 * half;
+        float al[8][CPL], xs[CPL];
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) xs[cc] = 0.f;
+        for (int cc = 0; cc < CPL; ++cc) xs[cc] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 8; ++r)
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) {
-                const float l2 = (16 * ti + r < Lc) ? la_r[r][cc] * kLog2e : 0.f;
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float l2 = (pb + r < Lc) ? la_r[r][cc] * kLog2e : 0.f;
                 xs[cc] += l2;
                 al[r][cc] = fexp2(l2);
             }
-        float e2[16][CPT], fB[CPT];
+        float e1[8][CPL], e2[8][CPL], fB[CPL];
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
+        for (int cc = 0; cc < CPL; ++cc) {
             float p = 1.f;
 #pragma unroll
-            for (int r = 15; r >= 0; --r) { e2[r][cc] = p; p *= al[r][cc]; }
-            fB[cc] = fexp2(-xs[cc]);
-            sDEC[ti * DK + cb + cc] = fexp2(xs[cc]);
+            for (int r = 0; r < 8; ++r) { p *= al[r][cc]; e1[r][cc] = p; }
+            const float own = p;
+            p = 1.f;
+#pragma unroll
+            for (int r = 7; r >= 0; --r) { e2[r][cc] = p; p *= al[r][cc]; }
+            const float other = __shfl_xor(own, 32, 64);
+            const float X = xs[cc] + __shfl_xor(xs[cc], 32, 64);
+            const float pre = half ? other : 1.f, post = half ? 1.f : other;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) { e1[r][cc] *= pre; e2[r][cc] *= post; }
+            fB[cc] = fexp2(-X);
+            if (half == 0) sDEC[ti * DK + cb + cc] = fexp2(X);
         }
-        float e1[CPT];
+        float ke2[CPL][8];
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) e1[cc] = 1.f;
-        float ke2[CPT][16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int pos = 16 * ti + r;
+        for (int r = 0; r < 8; ++r) {
+            const int pos = pb + r;
             const bool ok = pos < Lc;
-            float qe1[CPT], ke1[CPT], kb[CPT];
+            f32x4 qe1, ke1, kb;
 #pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) {
-                e1[cc] *= al[r][cc];
-                const float qv = ok ? word_elem<T>(qw_r[r], cc) : 0.f;
-                const float kv = ok ? word_elem<T>(kw_r[r], cc) : 0.f;
-                qe1[cc] = qv * e1[cc];
-                ke1[cc] = kv * e1[cc];
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float qv = ok ? lane_elem<T>(qw_r[r], cc) : 0.f;
+                const float kv = ok ? lane_elem<T>(kw_r[r], cc) : 0.f;
+                qe1[cc] = qv * e1[r][cc];
+                ke1[cc] = kv * e1[r][cc];
                 ke2[cc][r] = kv * e2[r][cc];
                 kb[cc] = ke2[cc][r] * fB[cc];
             }
             const int orow = pos * PL::LDK + cb;
-            if constexpr (CPT == 2) {
-                OP::put2(sQE1 + orow, qe1[0], qe1[CPT - 1]);
-                OP::put2(sKE1 + orow, ke1[0], ke1[CPT - 1]);
-                OP::put2(sKB + orow, kb[0], kb[CPT - 1]);
+            if constexpr (CPL == 4) {
+                OP::put4(sQE1 + orow, qe1);
+                OP::put4(sKE1 + orow, ke1);
+                OP::put4(sKB + orow, kb);
             } else {
-                OP::put(sQE1 + orow, qe1[0]);
-                OP::put(sKE1 + orow, ke1[0]);
-                OP::put(sKB + orow, kb[0]);
+                OP::put2(sQE1 + orow, qe1[0], qe1[1]);
+                OP::put2(sKE1 + orow, ke1[0], ke1[1]);
+                OP::put2(sKB + orow, kb[0], kb[1]);
             }
         }
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc)
+        for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
-            for (int r = 0; r < 16; r += 4) {
+            for (int r = 0; r < 8; r += 4) {
                 const f32x4 w4 = {ke2[cc][r], ke2[cc][r + 1], ke2[cc][r + 2], ke2[cc][r + 3]};
-                OP::put4(sKE2T + (cb + cc) * PL::LDC + 16 * ti + r, w4);
+                OP::put4(sKE2T + (cb + cc) * PL::LDC + pb + r, w4);
             }
         if (lane < 16) sBS[ti * 16 + lane] = (16 * ti + lane < Lc) ? beta_r : 0.f;
         wave_lds_sync();
@@ -420,7 +495,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int s = 4 * lg + e;
                 vp[e] = s <= l16 ? accP[e] : 0.f;
-                sMS[(ti * 16 + l16) * 17 + s] = s < l16 ? accM[e] : 0.f;
+                sMS[(ti * 16 + s) * PL::MSTR + l16] = s < l16 ? accM[e] : 0.f;   // M^T[s][r]
             }
             OP::put4(sPD + (ti * 16 + l16) * PL::LD16 + 4 * lg, vp);
         }
@@ -428,27 +503,48 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
 
         // A = (I + Diag(b) M)^{-1} Diag(b): lane j < 16 owns column j of the
         // inverse, right-looking substitution t_r = [r == j] - b_r sum_{s<r} M_rs t_s.
+        // Column s of M is row s of M^T; every load is independent of t, so all
+        // of them are issued before the dependent chain starts.
         if (lane < 16) {
-            const float* Mt = sMS + ti * 16 * 17;
-            const float* bt = sBS + ti * 16;
+            const float* MT = sMS + ti * 16 * PL::MSTR;
+            float bt[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(sBS + ti * 16 + 4 * q4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bt[4 * q4 + e] = b4[e];
+            }
+            // Rows of M^T are loaded two steps ahead of their use.
+            auto mrow = [&](int s, int q4) { return *reinterpret_cast<const f32x4*>(MT + s * PL::MSTR + 4 * q4); };
+            f32x4 r0[4], r1[4], r2[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) { r0[q4] = mrow(0, q4); r1[q4] = mrow(1, q4); }
             const int j = lane;
             float acc[16], t[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
+                if (s + 2 < 15) {
+#pragma unroll
+                    for (int q4 = (s + 3) / 4; q4 < 4; ++q4) r2[q4] = mrow(s + 2, q4);
+                }
                 t[s] = (s == j ? 1.f : 0.f) - bt[s] * acc[s];
 #pragma unroll
-                for (int r = s + 1; r < 16; ++r) acc[r] += Mt[r * 17 + s] * t[s];
+                for (int r = s + 1; r < 16; ++r) acc[r] += r0[r / 4][r % 4] * t[s];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) { r0[q4] = r1[q4]; r1[q4] = r2[q4]; }
             }
-            const float bj = bt[j];
+            float bj = bt[0];
+#pragma unroll
+            for (int s = 1; s < 16; ++s) bj = (s == j) ? bt[s] : bj;
 #pragma unroll
             for (int r = 0; r < 16; ++r) OP::put(sAD + (ti * 16 + r) * PL::LD16 + j, t[r] * bj);
         }
     };
 
     // ---- SD: state-dependent part of chunk c from buffer (c & 1).  Wave w = value columns.
-    auto sd = [&](int64_t c) {
+    auto sd = [&](int64_t c, f32x4 (&Sacc)[NCT]) {
         const unsigned char* buf = smem + (c & 1) * PL::BUF;
         const OT* sQE1 = reinterpret_cast<const OT*>(buf + PL::QE1);
         const OT* sKE1 = reinterpret_cast<const OT*>(buf + PL::KE1);
@@ -460,15 +556,30 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         const int64_t tok0 = seq0 + c * kC;
 #pragma unroll
         for (int i = 0; i < kTiles; ++i) {
+            using Seg = typename OP::Seg;
+            // All LDS operands of this tile, issued together.
+            Seg kseg[NCT], qseg[NCT], eseg[NCT];
+            f32x4 dec[NCT];
+            const OT* krow = sKE1 + (16 * i + l16) * PL::LDK;
+            const OT* qrow = sQE1 + (16 * i + l16) * PL::LDK;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) kseg[ct] = OP::seg(krow + 16 * ct);
+            const Seg aseg = OP::seg(sAD + (16 * i + l16) * PL::LD16);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) qseg[ct] = OP::seg(qrow + 16 * ct);
+            const Seg pseg = OP::seg(sPD + (16 * i + l16) * PL::LD16);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                eseg[ct] = OP::seg(sKE2T + (16 * ct + l16) * PL::LDC + 16 * i);
+                dec[ct] = *reinterpret_cast<const f32x4*>(sDEC + i * DK + 16 * ct + 4 * lg);
+            }
             Xop Sop[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) Sop[ct] = OP::cvt(Sacc[ct]);
             // U = V_i - (K e1)_i S   (D[r][v]: lane v = l16, rows r = 4 lg + e)
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const OT* krow = sKE1 + (16 * i + l16) * PL::LDK;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ct += 2)
-                acc = OP::lds_acc32(krow + 16 * ct, krow + 16 * (ct + 1), Sop[ct], Sop[ct + 1], acc);
+            for (int ct = 0; ct < NCT; ct += 2) acc = OP::seg_acc32(kseg[ct], kseg[ct + 1], Sop[ct], Sop[ct + 1], acc);
             f32x4 y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -477,55 +588,67 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             }
             // W = A U
             f32x4 w = {0.f, 0.f, 0.f, 0.f};
-            w = OP::lds_acc16(sAD + (16 * i + l16) * PL::LD16, OP::cvt(y), w);
+            w = OP::seg_acc16(aseg, OP::cvt(y), w);
             const Xop Wop = OP::cvt(w);
             // O^T = S^T (Q e1)^T + W^T P^T   (lane: row r = l16, columns 4 lg + e)
             f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
-            const OT* qrow = sQE1 + (16 * i + l16) * PL::LDK;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ct += 2)
-                oacc = OP::acc_lds32(Sop[ct], Sop[ct + 1], qrow + 16 * ct, qrow + 16 * (ct + 1), oacc);
-            oacc = OP::acc_lds16_k32(Wop, sPD + (16 * i + l16) * PL::LD16, oacc);
+            for (int ct = 0; ct < NCT; ct += 2) oacc = OP::acc_seg32(Sop[ct], Sop[ct + 1], qseg[ct], qseg[ct + 1], oacc);
+            oacc = OP::acc_seg16_k32(Wop, pseg, oacc);
+            // S <- Diag(2^X) S + (K e2)^T W   (lane v = l16, rows c = 16 ct + 4 lg + e)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = OP::seg_acc16(eseg[ct], Wop, Sacc[ct] * dec[ct]);
             const int pos = 16 * i + l16;
             if (pos < Lc) {
                 T* dst = o + ((tok0 + pos) * H + h) * DV + vcol + 4 * lg;
                 if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x2*>(dst) = OP::cvt(oacc);
                 else *reinterpret_cast<f32x4*>(dst) = oacc;
             }
-            // S <- Diag(2^X) S + (K e2)^T W   (lane v = l16, rows c = 16 ct + 4 lg + e)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const f32x4 dec = *reinterpret_cast<const f32x4*>(sDEC + i * DK + 16 * ct + 4 * lg);
-                f32x4 a = Sacc[ct] * dec;
-                a = OP::lds_acc16(sKE2T + (16 * ct + l16) * PL::LDC + 16 * i, Wop, a);
-                Sacc[ct] = a;
-            }
         }
     };
 
-    if (nchunks > 0) {
-        load_si(0);
-        load_v(0);
-        si(0);
-        if (nchunks > 1) load_si(1);
-        __syncthreads();
-        for (int64_t c = 0; c < nchunks; ++c) {
-            if (c + 1 < nchunks) {
-                si(c + 1);
-                if (c + 2 < nchunks) load_si(c + 2);
-            }
-            sd(c);
-            if (c + 1 < nchunks) load_v(c + 1);
+    // Waves 0..3 produce chunk c+1's state-independent results while waves
+    // 4..7 consume chunk c's.  Both roles pass the same barriers: one after
+    // the first chunk's results, then one per chunk.
+    if (wave < kSIW) {
+        if (nchunks > 0) {
+            load_si(0);
+            si(0);
+            if (nchunks > 1) load_si(1);
             __syncthreads();
+            for (int64_t c = 0; c < nchunks; ++c) {
+                if (c + 1 < nchunks) {
+                    si(c + 1);
+                    if (c + 2 < nchunks) load_si(c + 2);
+                }
+                __syncthreads();
+            }
         }
-    }
-
-    if (final_state != nullptr) {
-#pragma unroll
+    } else {
+        // This wave's state slab: Sacc[ct][e] = S[16 ct + 4 lg + e][vcol + l16].
+        f32x4 Sacc[NCT];
+        const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
+    #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
+    #pragma unroll
             for (int e = 0; e < 4; ++e)
-                final_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] = Sacc[ct][e];
+                Sacc[ct][e] = init_state ? init_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] : 0.f;
+        if (nchunks > 0) {
+            load_v(0);
+            __syncthreads();
+            for (int64_t c = 0; c < nchunks; ++c) {
+                sd(c, Sacc);
+                if (c + 1 < nchunks) load_v(c + 1);
+                __syncthreads();
+            }
+        }
+        if (final_state != nullptr) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    final_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] = Sacc[ct][e];
+        }
     }
 }
 
