@@ -73,22 +73,42 @@ print(json.dumps({"token_heads": done * 8, "seconds": dt}))
                       f"({r['seconds']:.1f} s, {th_per_s:.0f} token-heads/s, single thread)"}
 
 
+KERNEL_SOURCES = {
+    "prefill": ["gated_delta_rule_09_amd/csrc/kda_prefill.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
+                "gated_delta_rule_09_amd/csrc/kda_internal.h"],
+    "decode": ["gated_delta_rule_09_amd/csrc/kda_decode.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
+               "gated_delta_rule_09_amd/csrc/kda_internal.h"],
+}
+
+
+def kernel_digest(kernel: str) -> str:
+    """SHA-256 of a kernel's source files with comments and whitespace removed,
+    so that an edit of comments alone keeps a counter measurement valid while
+    any change of code voids it."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(rel.encode() + b"\0" + "".join(src.split()).encode() + b"\0")
+    return h.hexdigest()
+
+
 def measured_traffic(kernel: str, launch_ms: float):
     """HBM bytes per launch measured by the rocprofv3 FETCH_SIZE / WRITE_SIZE
     passes (calibrated against a plain copy), as GB/s over this run's launch
-    time; None when the kernel's source changed since the counters were
-    taken or no measurement is stored."""
-    import hashlib
+    time; None when the kernel's code changed since the counters were taken or
+    no measurement is stored."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f).get(kernel)
-    if not rec:
+    if not rec or rec.get("code_digest") != kernel_digest(kernel):
         return None
-    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
-            return None
     return round((rec["hbm_bytes_read"] + rec["hbm_bytes_written"]) / (launch_ms * 1e-3) / 1e9, 1)
 
 

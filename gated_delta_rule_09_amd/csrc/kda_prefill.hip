@@ -28,22 +28,31 @@
 // element); no pairwise exponentials are needed and no factor spans more than
 // one tile.
 //
-// Work decomposition: one workgroup of four waves per (sequence, head, block of
-// 64 value columns); the recurrence is independent across value columns.  Per
-// 64-token chunk two independent halves run in the same iteration:
-//   SI  (state-independent, chunk c+1): wave i owns tile i.  It forms the tile's
-//       decay factors and scaled operands, the tile's P and M (MFMA) and the
-//       16x16 inverse (fp32 substitution), and writes them to one of two LDS
-//       buffers.  Thread = (tile, two key channels): the running products are
-//       sequential in registers.
-//   SD  (state-dependent, chunk c): wave w owns value columns 16w .. 16w+15 and
+// Work decomposition: one workgroup of eight waves per (sequence, head, block
+// of 64 value columns); the recurrence is independent across value columns.
+// The waves take one of two roles, and in every chunk iteration both run at
+// once on different chunks:
+//   SI  (state-independent, waves 0-3, chunk c+1): wave i owns tile i.  A lane
+//       owns d_k/32 key channels of 8 of the tile's positions (lanes 0-31 the
+//       first 8, lanes 32-63 the last 8); the running products are formed in
+//       registers and joined across the two halves with one lane exchange.
+//       The wave writes the tile's scaled operands, its P and M (MFMA) and the
+//       16x16 inverse (fp32 substitution on 16 lanes) to one of two LDS
+//       buffers, selected by chunk parity.
+//   SD  (state-dependent, waves 4-7, chunk c): wave w owns 16 value columns and
 //       walks the chunk's four tiles.  Its slab of S, and U and W, live in MFMA
 //       accumulators and are fed back as MFMA operands directly (an accumulator
 //       tile holds 4 consecutive rows per lane, the K-layout of an operand);
 //       the LDS operands are read with the matching row permutation.
-// One barrier per chunk hands the SI buffer to SD.  Global loads run one chunk
-// ahead.  The two value-column workgroups of a head are placed 8 workgroups
-// apart so that they land on the same XCD and share its L2.
+// One workgroup barrier per chunk hands the SI buffer to SD and frees the
+// other buffer.  Global loads run one chunk ahead of their consumer.  The two
+// value-column workgroups of a head are placed 8 workgroups apart so that they
+// land on the same XCD and share its L2.
+//
+// One MFMA shape per accumulator chain: on gfx950, a 16x16x16 bf16 MFMA that
+// accumulates directly onto the result of a 16x16x32 bf16 MFMA was seen to
+// read stale accumulator registers.  Every chain that mixes K = 16 and K = 32
+// terms therefore issues the K = 16 term as a K = 32 MFMA with a zero half.
 //
 // Operand precision: bf16 inputs use bf16 MFMA operands with fp32 accumulation
 // (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16); fp32 inputs use
