@@ -48,3 +48,37 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 }  // namespace kda
+
+namespace kda {
+
+// Raw buffer access (gfx9 buffer descriptor, stride 0).  The base is
+// wave-uniform; `bytes` bounds the range: a load at a byte offset at or past
+// it returns zero and a store there is dropped.  Every offset that has to be
+// range-checked is passed as the per-lane offset (the scalar offset is zero).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_ld16(Rsrc r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_ld32(Rsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_ld64(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x4 buf_ld128(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st64(u32x2 x, Rsrc r, uint32_t off) {
+    typedef unsigned int v2u __attribute__((__vector_size__(8)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, x), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st128(u32x4 x, Rsrc r, uint32_t off) {
+    typedef unsigned int v4u __attribute__((__vector_size__(16)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), r, off, 0, 0);
+}
+
+}  // namespace kda

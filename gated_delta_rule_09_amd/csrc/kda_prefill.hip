@@ -59,6 +59,8 @@
 // v_mfma_f32_16x16x4_f32.  The state, the decay arithmetic and the inverse are
 // fp32 throughout.
 
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -76,6 +78,26 @@ constexpr int kBV = 16 * kSDW; // value columns per workgroup
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane (l ^ D) for D = 16 or 32 via the gfx950 row swaps (plain VALU,
+// no LDS round trip).  With both operands equal, v_permlane16_swap returns in
+// its first result the even row's value in the odd rows of each row pair and
+// in its second result the odd row's value in the even rows; v_permlane32_swap
+// does the same for the two halves of the wave.
+template <int D>
+__device__ __forceinline__ float xor_lanes(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const int lane = threadIdx.x & 63;
+    if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    } else if constexpr (D == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    } else {
+        return __shfl_xor(v, D, 64);
+    }
+}
 
 // Order this wave's earlier LDS writes before its later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -99,7 +121,10 @@ template <> struct Op<uint16_t> {    // bf16 operands
     typedef u32x2 Xop;               // an acc tile as a bf16 operand (4 values)
     static __device__ __forceinline__ Frag frag(const uint16_t* base, int ld, int k0) {
         const int lane = threadIdx.x & 63;
-        return *reinterpret_cast<const bf16x8*>(base + (lane & 15) * ld + 8 * (lane >> 4) + k0);
+        // Two 8-byte halves: rows are only 8-byte aligned (see the LDS plan).
+        const uint16_t* p = base + (lane & 15) * ld + 8 * (lane >> 4) + k0;
+        const u32x2 lo = ld4(p), hi = ld4(p + 4);
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
     static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
@@ -143,6 +168,21 @@ template <> struct Op<uint16_t> {    // bf16 operands
     static __device__ __forceinline__ Seg seg(const uint16_t* row) {
         return ld4(row + 4 * ((threadIdx.x & 63) >> 4));
     }
+    // Transposed segment of a row-major [K][16] block X (row stride ld): lane
+    // (g, t) gets X[4g + e][t], e = 0..3, i.e. the segment of row t of X^T.
+    // ds_read_b64_tr_b16 hands lane t of each 16-lane group element t % 4 of
+    // the 8-byte pieces read by lanes 4e + t / 4 of its group, so lane (g, t)
+    // points at row 4g + t / 4, columns 4 (t % 4) .. 4 (t % 4) + 3.
+    static __device__ __forceinline__ int seg_t_offset(int ld) {
+        const int lane = threadIdx.x & 63, t = lane & 15;
+        return (4 * (lane >> 4) + (t >> 2)) * ld + 4 * (t & 3);
+    }
+    static __device__ __forceinline__ Seg seg_t(const uint16_t* blk, int off, int /*ld*/) {
+        typedef short s16x4t __attribute__((ext_vector_type(4)));
+        const s16x4t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4t*)(blk + off));
+        return __builtin_bit_cast(Seg, r);
+    }
     static __device__ __forceinline__ f32x4 seg_acc16(Seg a, Xop xb, f32x4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, xb),
                                                          acc, 0, 0, 0);
@@ -177,6 +217,10 @@ template <> struct Op<uint16_t> {    // bf16 operands
         *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(x0, x1);
     }
     static __device__ __forceinline__ void put4(uint16_t* p, f32x4 x) { *reinterpret_cast<u32x2*>(p) = cvt(x); }
+    static __device__ __forceinline__ void put8(uint16_t* p, f32x4 a, f32x4 b) {   // two 8-byte stores
+        *reinterpret_cast<u32x2*>(p) = cvt(a);
+        *reinterpret_cast<u32x2*>(p + 4) = cvt(b);
+    }
 };
 
 template <> struct Op<float> {       // fp32 operands
@@ -218,6 +262,15 @@ template <> struct Op<float> {       // fp32 operands
     static __device__ __forceinline__ Seg seg(const float* row) {
         return *reinterpret_cast<const f32x4*>(row + 4 * ((threadIdx.x & 63) >> 4));
     }
+    // Transposed segment of a row-major [K][16] block X: lane (g, t) gets
+    // X[4g + e][t], e = 0..3 (four scalar reads; there is no 32-bit transpose read).
+    static __device__ __forceinline__ int seg_t_offset(int ld) {
+        const int lane = threadIdx.x & 63;
+        return 4 * (lane >> 4) * ld + (lane & 15);
+    }
+    static __device__ __forceinline__ Seg seg_t(const float* blk, int off, int ld) {
+        return f32x4{blk[off], blk[off + ld], blk[off + 2 * ld], blk[off + 3 * ld]};
+    }
     static __device__ __forceinline__ f32x4 seg_acc16(Seg a, Xop xb, f32x4 acc) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], xb[e], acc, 0, 0, 0);
@@ -240,6 +293,10 @@ template <> struct Op<float> {       // fp32 operands
         *reinterpret_cast<f32x2*>(p) = f32x2{x0, x1};
     }
     static __device__ __forceinline__ void put4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+    static __device__ __forceinline__ void put8(float* p, f32x4 a, f32x4 b) {
+        *reinterpret_cast<f32x4*>(p) = a;
+        *reinterpret_cast<f32x4*>(p + 4) = b;
+    }
 };
 
 // Raw input words: CPT packed elements (a bf16 pair, or one bf16 / fp32 element).
@@ -270,15 +327,24 @@ __device__ __forceinline__ float lane_elem(const uint32_t (&w)[N], int cc) {
 template <typename OT, int DK>
 struct Plan {
     static constexpr int ES = sizeof(OT);
-    static constexpr int PAD = 16 / ES;             // row padding: 16 bytes (keeps 16-byte row alignment)
+    // Row padding, chosen against LDS bank conflicts (32 banks of 4 bytes).
+    // The state-dependent waves read 8 bytes from each of 16 consecutive rows
+    // at one column: with bf16 rows of DK + 4 elements (DK/2 + 2 words) those
+    // land on 16 distinct bank pairs.  Such rows are only 8-byte aligned, so
+    // every access to them is at most 8 bytes wide.  fp32 rows keep 16 bytes
+    // of padding (16-byte aligned).
+    static constexpr int PAD = 4;
     static constexpr int LDK = DK + PAD;            // stride of [*, DK] rows
-    static constexpr int LDC = kC + PAD;            // stride of [*, C] rows
-    static constexpr int LD16 = 16 + PAD;           // stride of 16x16 blocks
+    // Stride of the k * e2 rows (72 words for DK = 128 bf16 or DK = 64 fp32),
+    // read only through transposed segments: the four rows one lane group
+    // reads then fall 8 banks apart.
+    static constexpr int LDK2 = DK + 32 / ES;
+    static constexpr int LD16 = 16 + PAD;           // stride of 16x16 blocks (10 words for bf16)
     // one buffer
     static constexpr int QE1 = 0;                                  // [C][LDK]   q * e1
     static constexpr int KE1 = QE1 + kC * LDK * ES;                // [C][LDK]   k * e1
-    static constexpr int KE2T = KE1 + kC * LDK * ES;               // [DK][LDC]  (k * e2)^T
-    static constexpr int PD = KE2T + DK * LDC * ES;                // [4][16][LD16] P per tile
+    static constexpr int KE2 = KE1 + kC * LDK * ES;                // [C][LDK2]  k * e2
+    static constexpr int PD = KE2 + kC * LDK2 * ES;                // [4][16][LD16] P per tile
     static constexpr int AD = PD + kTiles * 16 * LD16 * ES;        // [4][16][LD16] A per tile
     static constexpr int DEC = AD + kTiles * 16 * LD16 * ES;       // [4][DK] fp32 2^X per tile
     static constexpr int BUF = DEC + kTiles * DK * 4;
@@ -303,12 +369,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     using PL = Plan<OT, DK>;
     using Xop = typename OP::Xop;
     constexpr int KS = OP::KS;
-    constexpr int CPL = DK / 32;          // SI: key channels per lane (lane = channel group x half tile)
+    constexpr int CPL = 8;                // SI: key channels per lane (16-byte loads of bf16 q, k)
+    constexpr int LPR = DK / CPL;         // SI: lanes per token row
+    constexpr int NG = 64 / LPR;          // SI: position groups of a tile
+    constexpr int RP = 16 / NG;           // SI: consecutive tile positions per lane
     constexpr int QWN = CPL * (int)sizeof(T) / 4;   // 32-bit words holding CPL q (or k) elements
     constexpr int NCT = DK / 16;          // 16-row channel tiles of the state
     constexpr int NKS = DK / KS;          // K-steps of the Gram products
     constexpr int NV = DV / kBV;          // value-column workgroups per (sequence, head)
-    static_assert(CPL == 2 || CPL == 4, "SI mapping");
+    static_assert((LPR == 8 || LPR == 16) && RP >= 2, "SI mapping");
     static_assert(NV == 1 || NV == 2, "value blocking");
 
     // Workgroup -> (unit = sequence * H + head, value block).  With two value
@@ -332,13 +401,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     OT* sKB = reinterpret_cast<OT*>(smem + PL::KB);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l16 = lane & 15;
     const int lg = lane >> 4;
     const int vcol = vblk * kBV + 16 * (wave - kSIW);   // SD waves: first value column
-    const int cb = (lane & 31) * CPL;            // SI: first key channel of this lane
-    const int half = lane >> 5;                  // SI: which 8 positions of the tile
+    const int tro = OP::seg_t_offset(PL::LDK2);          // SD: lane offset of transposed reads
+    const int cb = (lane % LPR) * CPL;           // SI: first key channel of this lane
+    const int pg = lane / LPR;                   // SI: position group (positions RP pg .. RP pg + RP - 1)
 
     // Sequence range, clamped so malformed offsets cannot address out of range.
     int64_t seq0 = 0, seq1 = total_T;
@@ -351,58 +421,63 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     const int64_t len = seq1 - seq0;
     const int64_t nchunks = (len + kC - 1) / kC;
 
-    // ---- prefetch registers (one chunk ahead).  Positions past a chunk's end
-    // are clamped to its last token (a valid address) and zeroed when used.
-    float la_r[8][CPL];
-    uint32_t qw_r[8][QWN], kw_r[8][QWN];
+    // ---- prefetch registers (one chunk ahead).  Loads go through buffer
+    // descriptors whose range ends after the chunk's last valid token, so rows
+    // past a sequence's end read as zero (decay 1, key, query, value and beta
+    // 0) and output rows past it are not written.
+    float la_r[RP][CPL];
+    uint32_t qw_r[RP][QWN], kw_r[RP][QWN];
     float beta_r;
-    uint32_t v_r[kTiles][4];     // v[16 i + 4 lg + e][vcol + l16]
+    uint32_t v_r[kTiles][4];     // v[16 i + 4 lg + e][vcol + l16], raw words
     auto chunk_len = [&](int64_t c) { return (int)((len - c * kC) < kC ? (len - c * kC) : kC); };
-    // One 64-bit base per chunk, then 32-bit offsets; rows past the chunk's
-    // end are clamped to its last token.
+    // Rows of the [tokens, H] layout from a head's first valid row to the end
+    // of its last valid row: (Lc - 1) * H + 1.
+    // Beyond the last chunk the range is empty (every load returns zero and
+    // touches no memory), so prefetches can be issued unconditionally and the
+    // compiler's in-order wait counts never include them.
+    auto valid_rows = [&](int64_t c) {
+        return c < nchunks ? (uint32_t)(chunk_len(c) - 1) * (uint32_t)H + 1u : 0u;
+    };
+    auto row_of = [&](int64_t c) { return (seq0 + (c < nchunks ? c : 0) * kC) * H + h; };
+    const uint32_t p0 = 16 * wave + RP * pg;    // SI: chunk position of this lane's first row
     auto load_si = [&](int64_t c) {
-        const int pmax = chunk_len(c) - 1 - 16 * wave - 8 * half;   // last valid row of this lane's 8 (may be < 0)
-        const int64_t row0 = (seq0 + c * kC + 16 * wave + 8 * half) * H + h;
-        const float* la0 = log_alpha + row0 * DK + cb;
-        const T* q0 = q + row0 * DK + cb;
-        const T* k0 = k + row0 * DK + cb;
-        const int stride = H * DK;
+        const uint32_t nr = valid_rows(c);
+        const int64_t row0 = row_of(c);
+        const Rsrc rla = make_rsrc(log_alpha + row0 * DK, nr * (DK * 4));
+        const Rsrc rq = make_rsrc(q + row0 * DK, nr * (DK * (uint32_t)sizeof(T)));
+        const Rsrc rk = make_rsrc(k + row0 * DK, nr * (DK * (uint32_t)sizeof(T)));
+        const uint32_t rs = (uint32_t)H * DK;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int off = (r < pmax ? r : pmax) * stride;
-            if constexpr (CPL == 4) {
-                const f32x4 la4 = *reinterpret_cast<const f32x4*>(la0 + off);
+        for (int r = 0; r < RP; ++r) {
+            const uint32_t el = (p0 + r) * rs + cb;
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) la_r[r][cc] = la4[cc];
-            } else {
-                const f32x2 la2 = *reinterpret_cast<const f32x2*>(la0 + off);
+            for (int u = 0; u < CPL / 4; ++u) {
+                const u32x4 a = buf_ld128(rla, el * 4 + 16 * u);
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) la_r[r][cc] = la2[cc];
+                for (int j = 0; j < 4; ++j) la_r[r][4 * u + j] = __uint_as_float(a[j]);
             }
-            if constexpr (QWN == 2) {
-                const u32x2 qv = *reinterpret_cast<const u32x2*>(q0 + off);
-                const u32x2 kv = *reinterpret_cast<const u32x2*>(k0 + off);
-                qw_r[r][0] = qv[0]; qw_r[r][QWN - 1] = qv[1];
-                kw_r[r][0] = kv[0]; kw_r[r][QWN - 1] = kv[1];
-            } else {
-                qw_r[r][0] = *reinterpret_cast<const uint32_t*>(q0 + off);
-                kw_r[r][0] = *reinterpret_cast<const uint32_t*>(k0 + off);
+#pragma unroll
+            for (int u = 0; u < QWN / 4; ++u) {
+                const u32x4 qv = buf_ld128(rq, el * (uint32_t)sizeof(T) + 16 * u);
+                const u32x4 kv = buf_ld128(rk, el * (uint32_t)sizeof(T) + 16 * u);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { qw_r[r][4 * u + j] = qv[j]; kw_r[r][4 * u + j] = kv[j]; }
             }
         }
-        const int pb = chunk_len(c) - 1 - 16 * wave;
-        beta_r = beta[(seq0 + c * kC + 16 * wave) * H + h + (l16 < pb ? l16 : pb) * H];
+        beta_r = __uint_as_float(buf_ld32(make_rsrc(beta + row0, nr * 4), (16 * wave + l16) * (uint32_t)H * 4));
     };
-    auto load_v = [&](int64_t c) {
-        const int pmax = chunk_len(c) - 1;
-        const T* v0 = v + ((seq0 + c * kC) * H + h) * DV + vcol + l16;
-        const int stride = H * DV;
+    auto v_rsrc = [&](int64_t c) {
+        return make_rsrc(v + row_of(c) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)));
+    };
+    auto load_v_tile = [&](Rsrc rv, int i) {
+        const uint32_t rs = (uint32_t)H * DV;
 #pragma unroll
-        for (int i = 0; i < kTiles; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int p = 16 * i + 4 * lg + e;
-                v_r[i][e] = load_word<T, 1>(v0 + (p < pmax ? p : pmax) * stride);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t el = (16 * i + 4 * lg + e) * rs + l16;
+            // Raw words: widening happens at the use, so that the load is not waited for here.
+            if constexpr (sizeof(T) == 2) v_r[i][e] = buf_ld16(rv, el * 2);
+            else v_r[i][e] = buf_ld32(rv, el * 4);
+        }
     };
 
     // ---- SI: state-independent results of chunk c into buffer (c & 1).  Wave i = tile i.
@@ -410,80 +485,81 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         unsigned char* buf = smem + (c & 1) * PL::BUF;
         OT* sQE1 = reinterpret_cast<OT*>(buf + PL::QE1);
         OT* sKE1 = reinterpret_cast<OT*>(buf + PL::KE1);
-        OT* sKE2T = reinterpret_cast<OT*>(buf + PL::KE2T);
+        OT* sKE2 = reinterpret_cast<OT*>(buf + PL::KE2);
         OT* sPD = reinterpret_cast<OT*>(buf + PL::PD);
         OT* sAD = reinterpret_cast<OT*>(buf + PL::AD);
         float* sDEC = reinterpret_cast<float*>(buf + PL::DEC);
-        const int Lc = chunk_len(c);
         const int ti = wave;
-        // Lane = (channel group cb .. cb+CPL-1, positions pb .. pb+7 of the tile).
+        // Lane = (key channels cb .. cb+7; tile positions pb .. pb+RP-1).
         // alpha = 2^{l2}; e1 = prefix products over the tile, e2 = suffix
-        // products excluding r.  Each half forms its own running products; the
-        // halves then exchange their totals.
-        const int pb = 16 * ti + 8 * half;
-        float al[8][CPL], xs[CPL];
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) xs[cc] = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const float l2 = (pb + r < Lc) ? la_r[r][cc] * kLog2e : 0.f;
-                xs[cc] += l2;
-                al[r][cc] = fexp2(l2);
-            }
-        float e1[8][CPL], e2[8][CPL], fB[CPL];
+        // products excluding r, dec = the product over the whole tile.  Each
+        // lane forms the running products of its RP positions; a butterfly
+        // over the position groups then supplies the product of the groups
+        // before (pre) and after (post) this lane's, and the tile total.
+        const int pb = (int)p0;
+        float e1[RP][CPL], e2[RP][CPL], fB[CPL], dec[CPL], pre[CPL], post[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
+            float al[RP];
+#pragma unroll
+            for (int r = 0; r < RP; ++r) al[r] = fexp2(la_r[r][cc] * kLog2e);
             float p = 1.f;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) { p *= al[r][cc]; e1[r][cc] = p; }
-            const float own = p;
-            p = 1.f;
+            for (int r = 0; r < RP; ++r) { p *= al[r]; e1[r][cc] = p; }
+            float sfx = 1.f;
 #pragma unroll
-            for (int r = 7; r >= 0; --r) { e2[r][cc] = p; p *= al[r][cc]; }
-            const float other = __shfl_xor(own, 32, 64);
-            const float X = xs[cc] + __shfl_xor(xs[cc], 32, 64);
-            const float pre = half ? other : 1.f, post = half ? 1.f : other;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) { e1[r][cc] *= pre; e2[r][cc] *= post; }
-            fB[cc] = fexp2(-X);
-            if (half == 0) sDEC[ti * DK + cb + cc] = fexp2(X);
+            for (int r = RP - 1; r >= 0; --r) { e2[r][cc] = sfx; sfx *= al[r]; }
+            dec[cc] = p;
+            pre[cc] = 1.f;
+            post[cc] = 1.f;
         }
-        float ke2[CPL][8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int pos = pb + r;
-            const bool ok = pos < Lc;
-            f32x4 qe1, ke1, kb;
+        // Butterfly over the position groups (block of LPR lanes, then 2 LPR, ...).
+        auto level = [&](auto dtag) {
+            constexpr int D = decltype(dtag)::value;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
-                const float qv = ok ? lane_elem<T>(qw_r[r], cc) : 0.f;
-                const float kv = ok ? lane_elem<T>(kw_r[r], cc) : 0.f;
-                qe1[cc] = qv * e1[r][cc];
-                ke1[cc] = kv * e1[r][cc];
-                ke2[cc][r] = kv * e2[r][cc];
-                kb[cc] = ke2[cc][r] * fB[cc];
+                const float other = xor_lanes<D>(dec[cc]);   // product of the partner block
+                if (lane & D) pre[cc] *= other; else post[cc] *= other;
+                dec[cc] *= other;                            // same value in both blocks
             }
-            const int orow = pos * PL::LDK + cb;
-            if constexpr (CPL == 4) {
-                OP::put4(sQE1 + orow, qe1);
-                OP::put4(sKE1 + orow, ke1);
-                OP::put4(sKB + orow, kb);
-            } else {
-                OP::put2(sQE1 + orow, qe1[0], qe1[1]);
-                OP::put2(sKE1 + orow, ke1[0], ke1[1]);
-                OP::put2(sKB + orow, kb[0], kb[1]);
-            }
+        };
+        if constexpr (LPR == 8) level(std::integral_constant<int, 8>{});
+        level(std::integral_constant<int, 16>{});
+        level(std::integral_constant<int, 32>{});
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+#pragma unroll
+            for (int r = 0; r < RP; ++r) { e1[r][cc] *= pre[cc]; e2[r][cc] *= post[cc]; }
+            fB[cc] = __builtin_amdgcn_rcpf(dec[cc]);
+        }
+        if (pg == 0) {
+#pragma unroll
+            for (int u = 0; u < CPL / 4; ++u)
+                *reinterpret_cast<f32x4*>(sDEC + ti * DK + cb + 4 * u) =
+                    f32x4{dec[4 * u], dec[4 * u + 1], dec[4 * u + 2], dec[4 * u + 3]};
         }
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
+        for (int r = 0; r < RP; ++r) {
+            const int orow = (pb + r) * PL::LDK + cb;
+            f32x4 qe1[2], ke1[2], ke2[2], kb[2];
 #pragma unroll
-            for (int r = 0; r < 8; r += 4) {
-                const f32x4 w4 = {ke2[cc][r], ke2[cc][r + 1], ke2[cc][r + 2], ke2[cc][r + 3]};
-                OP::put4(sKE2T + (cb + cc) * PL::LDC + pb + r, w4);
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float qv = lane_elem<T>(qw_r[r], cc);
+                const float kv = lane_elem<T>(kw_r[r], cc);
+                qe1[cc / 4][cc % 4] = qv * e1[r][cc];
+                ke1[cc / 4][cc % 4] = kv * e1[r][cc];
+                ke2[cc / 4][cc % 4] = kv * e2[r][cc];
+                kb[cc / 4][cc % 4] = ke2[cc / 4][cc % 4] * fB[cc];
             }
-        if (lane < 16) sBS[ti * 16 + lane] = (16 * ti + lane < Lc) ? beta_r : 0.f;
+            OP::put8(sQE1 + orow, qe1[0], qe1[1]);
+            OP::put8(sKE1 + orow, ke1[0], ke1[1]);
+            OP::put8(sKE2 + (pb + r) * PL::LDK2 + cb, ke2[0], ke2[1]);
+            OP::put8(sKB + orow, kb[0], kb[1]);
+        }
+        if (lane < 16) sBS[ti * 16 + lane] = beta_r;
+        // The prefetch registers are free again: load the next chunk now, so
+        // that its loads are in flight during the products and the inverse.
+        load_si(c + 1);
         wave_lds_sync();
 
         // P and M of the tile, transposed (D[s][r] = sum_c Kb[s][c] X[r][c]):
@@ -554,15 +630,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
 
     // ---- SD: state-dependent part of chunk c from buffer (c & 1).  Wave w = value columns.
     auto sd = [&](int64_t c, f32x4 (&Sacc)[NCT]) {
+        const Rsrc rv_next = v_rsrc(c + 1);
         const unsigned char* buf = smem + (c & 1) * PL::BUF;
         const OT* sQE1 = reinterpret_cast<const OT*>(buf + PL::QE1);
         const OT* sKE1 = reinterpret_cast<const OT*>(buf + PL::KE1);
-        const OT* sKE2T = reinterpret_cast<const OT*>(buf + PL::KE2T);
+        const OT* sKE2 = reinterpret_cast<const OT*>(buf + PL::KE2);
         const OT* sPD = reinterpret_cast<const OT*>(buf + PL::PD);
         const OT* sAD = reinterpret_cast<const OT*>(buf + PL::AD);
         const float* sDEC = reinterpret_cast<const float*>(buf + PL::DEC);
-        const int Lc = chunk_len(c);
-        const int64_t tok0 = seq0 + c * kC;
+        const Rsrc ro = make_rsrc(o + row_of(c) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)));
 #pragma unroll
         for (int i = 0; i < kTiles; ++i) {
             using Seg = typename OP::Seg;
@@ -579,7 +655,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             const Seg pseg = OP::seg(sPD + (16 * i + l16) * PL::LD16);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                eseg[ct] = OP::seg(sKE2T + (16 * ct + l16) * PL::LDC + 16 * i);
+                eseg[ct] = OP::seg_t(sKE2 + 16 * i * PL::LDK2 + 16 * ct, tro, PL::LDK2);
                 dec[ct] = *reinterpret_cast<const f32x4*>(sDEC + i * DK + 16 * ct + 4 * lg);
             }
             Xop Sop[NCT];
@@ -592,9 +668,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             f32x4 y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float vv = (16 * i + 4 * lg + e < Lc) ? word_elem<T>(v_r[i][e], 0) : 0.f;
-                y[e] = vv - acc[e];
+                y[e] = word_elem<T>(v_r[i][e], 0) - acc[e];
             }
+            // v of this tile is consumed: load the same tile of the next chunk.
+            load_v_tile(rv_next, i);
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch here, early in the chunk
             // W = A U
             f32x4 w = {0.f, 0.f, 0.f, 0.f};
             w = OP::seg_acc16(aseg, OP::cvt(y), w);
@@ -607,12 +685,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             // S <- Diag(2^X) S + (K e2)^T W   (lane v = l16, rows c = 16 ct + 4 lg + e)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = OP::seg_acc16(eseg[ct], Wop, Sacc[ct] * dec[ct]);
-            const int pos = 16 * i + l16;
-            if (pos < Lc) {
-                T* dst = o + ((tok0 + pos) * H + h) * DV + vcol + 4 * lg;
-                if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x2*>(dst) = OP::cvt(oacc);
-                else *reinterpret_cast<f32x4*>(dst) = oacc;
-            }
+            const uint32_t ooff = ((16 * i + l16) * (uint32_t)H * DV + 4 * lg) * (uint32_t)sizeof(T);
+            if constexpr (sizeof(T) == 2) buf_st64(OP::cvt(oacc), ro, ooff);
+            else buf_st128(__builtin_bit_cast(u32x4, oacc), ro, ooff);
         }
     };
 
@@ -623,13 +698,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         if (nchunks > 0) {
             load_si(0);
             si(0);
-            if (nchunks > 1) load_si(1);
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
-                if (c + 1 < nchunks) {
-                    si(c + 1);
-                    if (c + 2 < nchunks) load_si(c + 2);
-                }
+                if (c + 1 < nchunks) si(c + 1);
                 __syncthreads();
             }
         }
@@ -643,11 +714,14 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             for (int e = 0; e < 4; ++e)
                 Sacc[ct][e] = init_state ? init_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] : 0.f;
         if (nchunks > 0) {
-            load_v(0);
+            {
+                const Rsrc rv0 = v_rsrc(0);
+#pragma unroll
+                for (int i = 0; i < kTiles; ++i) load_v_tile(rv0, i);
+            }
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
                 sd(c, Sacc);
-                if (c + 1 < nchunks) load_v(c + 1);
                 __syncthreads();
             }
         }
