@@ -440,12 +440,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     };
     auto row_of = [&](int64_t c) { return (seq0 + (c < nchunks ? c : 0) * kC) * H + h; };
     const uint32_t p0 = 16 * wave + RP * pg;    // SI: chunk position of this lane's first row
-    auto load_si = [&](int64_t c) {
-        const uint32_t nr = valid_rows(c);
-        const int64_t row0 = row_of(c);
-        const Rsrc rla = make_rsrc(log_alpha + row0 * DK, nr * (DK * 4));
-        const Rsrc rq = make_rsrc(q + row0 * DK, nr * (DK * (uint32_t)sizeof(T)));
-        const Rsrc rk = make_rsrc(k + row0 * DK, nr * (DK * (uint32_t)sizeof(T)));
+    // The state-independent prefetch comes in two parts, each issued as soon
+    // as its registers are free: log-decay after the exponentials, q, k and
+    // beta after the products of the tile.
+    auto load_la = [&](int64_t c) {
+        const Rsrc rla = make_rsrc(log_alpha + row_of(c) * DK, valid_rows(c) * (DK * 4));
         const uint32_t rs = (uint32_t)H * DK;
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
@@ -456,6 +455,17 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) la_r[r][4 * u + j] = __uint_as_float(a[j]);
             }
+        }
+    };
+    auto load_qk = [&](int64_t c) {
+        const uint32_t nr = valid_rows(c);
+        const int64_t row0 = row_of(c);
+        const Rsrc rq = make_rsrc(q + row0 * DK, nr * (DK * (uint32_t)sizeof(T)));
+        const Rsrc rk = make_rsrc(k + row0 * DK, nr * (DK * (uint32_t)sizeof(T)));
+        const uint32_t rs = (uint32_t)H * DK;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            const uint32_t el = (p0 + r) * rs + cb;
 #pragma unroll
             for (int u = 0; u < QWN / 4; ++u) {
                 const u32x4 qv = buf_ld128(rq, el * (uint32_t)sizeof(T) + 16 * u);
@@ -513,6 +523,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             pre[cc] = 1.f;
             post[cc] = 1.f;
         }
+        load_la(c + 1);
+        __builtin_amdgcn_sched_barrier(0);
         // Butterfly over the position groups (block of LPR lanes, then 2 LPR, ...).
         auto level = [&](auto dtag) {
             constexpr int D = decltype(dtag)::value;
@@ -557,9 +569,6 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             OP::put8(sKB + orow, kb[0], kb[1]);
         }
         if (lane < 16) sBS[ti * 16 + lane] = beta_r;
-        // The prefetch registers are free again: load the next chunk now, so
-        // that its loads are in flight during the products and the inverse.
-        load_si(c + 1);
         wave_lds_sync();
 
         // P and M of the tile, transposed (D[s][r] = sum_c Kb[s][c] X[r][c]):
@@ -584,6 +593,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             }
             OP::put4(sPD + (ti * 16 + l16) * PL::LD16 + 4 * lg, vp);
         }
+        load_qk(c + 1);
+        __builtin_amdgcn_sched_barrier(0);
         wave_lds_sync();
 
         // A = (I + Diag(b) M)^{-1} Diag(b): lane j < 16 owns column j of the
@@ -696,7 +707,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     // the first chunk's results, then one per chunk.
     if (wave < kSIW) {
         if (nchunks > 0) {
-            load_si(0);
+            load_la(0);
+            load_qk(0);
             si(0);
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
