@@ -99,6 +99,20 @@ __device__ __forceinline__ float xor_lanes(float v) {
     }
 }
 
+// Value of lane Q of this lane's quad (DPP quad_perm broadcast).
+template <int Q>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x55 * Q, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float quad_bcast(float v, int q) {   // q is a constant after unrolling
+    switch (q) {
+        case 0: return quad_bcast<0>(v);
+        case 1: return quad_bcast<1>(v);
+        case 2: return quad_bcast<2>(v);
+        default: return quad_bcast<3>(v);
+    }
+}
+
 // Order this wave's earlier LDS writes before its later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
@@ -589,7 +603,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int s = 4 * lg + e;
                 vp[e] = s <= l16 ? accP[e] : 0.f;
-                sMS[(ti * 16 + s) * PL::MSTR + l16] = s < l16 ? accM[e] : 0.f;   // M^T[s][r]
+                // M^T[s][r], columns in (r % 4, r / 4) order
+                sMS[(ti * 16 + s) * PL::MSTR + 4 * (l16 & 3) + (l16 >> 2)] = s < l16 ? accM[e] : 0.f;
             }
             OP::put4(sPD + (ti * 16 + l16) * PL::LD16 + 4 * lg, vp);
         }
@@ -597,12 +612,17 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         __builtin_amdgcn_sched_barrier(0);
         wave_lds_sync();
 
-        // A = (I + Diag(b) M)^{-1} Diag(b): lane j < 16 owns column j of the
-        // inverse, right-looking substitution t_r = [r == j] - b_r sum_{s<r} M_rs t_s.
-        // Column s of M is row s of M^T; every load is independent of t, so all
-        // of them are issued before the dependent chain starts.
-        if (lane < 16) {
-            const float* MT = sMS + ti * 16 * PL::MSTR;
+        // A = (I + Diag(b) M)^{-1} Diag(b) by right-looking substitution on
+        // all 64 lanes: lane = (column j = lane / 4, row residue q = lane % 4)
+        // and holds rows r = 4 m + q, m = 0..3, of column j of X = (I +
+        // Diag(b) M)^{-1}:  x_s = [s == j] - b_s sum_{s' < s} M_{s s'} x_{s'}.
+        // At step s the lane that owns row s forms x_s, a quad broadcast (DPP)
+        // hands it to the other three lanes of its column, and every lane adds
+        // M_{r s} x_s to its rows.  Row s of M^T is stored with its columns in
+        // (q, m) order, so one 16-byte read gives a lane its four M_{r s}.
+        {
+            const int j = lane >> 2, q = lane & 3;
+            const float* MT = sMS + ti * 16 * PL::MSTR + 4 * q;
             float bt[16];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -610,32 +630,25 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bt[4 * q4 + e] = b4[e];
             }
-            // Rows of M^T are loaded two steps ahead of their use.
-            auto mrow = [&](int s, int q4) { return *reinterpret_cast<const f32x4*>(MT + s * PL::MSTR + 4 * q4); };
-            f32x4 r0[4], r1[4], r2[4];
+            f32x4 mr[16];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) { r0[q4] = mrow(0, q4); r1[q4] = mrow(1, q4); }
-            const int j = lane;
-            float acc[16], t[16];
+            for (int s2 = 0; s2 < 16; ++s2) mr[s2] = *reinterpret_cast<const f32x4*>(MT + s2 * PL::MSTR);
+            float acc[4], xs[4], one[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+            for (int m = 0; m < 4; ++m) { acc[m] = 0.f; xs[m] = 0.f; one[m] = (4 * m + q == j) ? 1.f : 0.f; }
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                if (s + 2 < 15) {
+            for (int s2 = 0; s2 < 16; ++s2) {
+                const int ms = s2 >> 2, qs = s2 & 3;
+                const float cand = fmaf(-bt[s2], acc[ms], one[ms]);   // x_s in the lanes with q == s % 4
+                if (q == qs) xs[ms] = cand;
+                const float x = quad_bcast(cand, qs);
 #pragma unroll
-                    for (int q4 = (s + 3) / 4; q4 < 4; ++q4) r2[q4] = mrow(s + 2, q4);
-                }
-                t[s] = (s == j ? 1.f : 0.f) - bt[s] * acc[s];
-#pragma unroll
-                for (int r = s + 1; r < 16; ++r) acc[r] += r0[r / 4][r % 4] * t[s];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) { r0[q4] = r1[q4]; r1[q4] = r2[q4]; }
+                for (int m = 0; m < 4; ++m)
+                    if (4 * m + 3 > s2) acc[m] = fmaf(mr[s2][m], x, acc[m]);
             }
-            float bj = bt[0];
+            const float bj = sBS[ti * 16 + j];
 #pragma unroll
-            for (int s = 1; s < 16; ++s) bj = (s == j) ? bt[s] : bj;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) OP::put(sAD + (ti * 16 + r) * PL::LD16 + j, t[r] * bj);
+            for (int m = 0; m < 4; ++m) OP::put(sAD + (ti * 16 + 4 * m + q) * PL::LD16 + j, xs[m] * bj);
         }
     };
 
