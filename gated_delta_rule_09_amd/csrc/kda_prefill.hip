@@ -79,23 +79,26 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of lane (l ^ D) for D = 16 or 32 via the gfx950 row swaps (plain VALU,
-// no LDS round trip).  With both operands equal, v_permlane16_swap returns in
-// its first result the even row's value in the odd rows of each row pair and
-// in its second result the odd row's value in the even rows; v_permlane32_swap
-// does the same for the two halves of the wave.
+// For blocks of D lanes (D = 8, 16, 32) paired as (2b, 2b + 1): the value
+// that the lower and the upper block of this lane's pair hold, in every lane
+// of the pair.  For D = 16 and 32 this is one gfx950 row swap (plain VALU):
+// with both operands equal, v_permlane16_swap returns the even row's value in
+// its first result and the odd row's in its second, in both rows of a pair;
+// v_permlane32_swap does the same for the two halves of the wave.
+struct LoHi { float lo, hi; };
 template <int D>
-__device__ __forceinline__ float xor_lanes(float v) {
+__device__ __forceinline__ LoHi block_pair(float v) {
     const uint32_t u = __float_as_uint(v);
-    const int lane = threadIdx.x & 63;
     if constexpr (D == 16) {
         const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+        return {__uint_as_float(r[0]), __uint_as_float(r[1])};
     } else if constexpr (D == 32) {
         const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        return __uint_as_float((lane & 32) ? r[0] : r[1]);
+        return {__uint_as_float(r[0]), __uint_as_float(r[1])};
     } else {
-        return __shfl_xor(v, D, 64);
+        const float other = __shfl_xor(v, D, 64);
+        const bool upper = (threadIdx.x & D) != 0;
+        return {upper ? other : v, upper ? v : other};
     }
 }
 
@@ -110,6 +113,25 @@ __device__ __forceinline__ float quad_bcast(float v, int q) {   // q is a consta
         case 1: return quad_bcast<1>(v);
         case 2: return quad_bcast<2>(v);
         default: return quad_bcast<3>(v);
+    }
+}
+
+// Value of lane K of this lane's 16-lane row (DPP row_newbcast, gfx90a and
+// later); folded by the compiler into the consuming VALU instruction.
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_bcast(float v, int k) {   // k is a constant after unrolling
+    switch (k) {
+        case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
+        case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
+        case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
+        case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
+        case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
+        case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
+        case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
+        case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
     }
 }
 
@@ -471,24 +493,25 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             }
         }
     };
-    auto load_qk = [&](int64_t c) {
-        const uint32_t nr = valid_rows(c);
+    struct QKRes { Rsrc q, k; };
+    auto qk_rsrc = [&](int64_t c) {
+        const uint32_t nb = valid_rows(c) * (DK * (uint32_t)sizeof(T));
         const int64_t row0 = row_of(c);
-        const Rsrc rq = make_rsrc(q + row0 * DK, nr * (DK * (uint32_t)sizeof(T)));
-        const Rsrc rk = make_rsrc(k + row0 * DK, nr * (DK * (uint32_t)sizeof(T)));
-        const uint32_t rs = (uint32_t)H * DK;
+        return QKRes{make_rsrc(q + row0 * DK, nb), make_rsrc(k + row0 * DK, nb)};
+    };
+    auto load_qk_row = [&](const QKRes& rr, int r) {
+        const uint32_t el = (p0 + r) * ((uint32_t)H * DK) + cb;
 #pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            const uint32_t el = (p0 + r) * rs + cb;
+        for (int u = 0; u < QWN / 4; ++u) {
+            const u32x4 qv = buf_ld128(rr.q, el * (uint32_t)sizeof(T) + 16 * u);
+            const u32x4 kv = buf_ld128(rr.k, el * (uint32_t)sizeof(T) + 16 * u);
 #pragma unroll
-            for (int u = 0; u < QWN / 4; ++u) {
-                const u32x4 qv = buf_ld128(rq, el * (uint32_t)sizeof(T) + 16 * u);
-                const u32x4 kv = buf_ld128(rk, el * (uint32_t)sizeof(T) + 16 * u);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { qw_r[r][4 * u + j] = qv[j]; kw_r[r][4 * u + j] = kv[j]; }
-            }
+            for (int j = 0; j < 4; ++j) { qw_r[r][4 * u + j] = qv[j]; kw_r[r][4 * u + j] = kv[j]; }
         }
-        beta_r = __uint_as_float(buf_ld32(make_rsrc(beta + row0, nr * 4), (16 * wave + l16) * (uint32_t)H * 4));
+    };
+    auto load_beta = [&](int64_t c) {
+        beta_r = __uint_as_float(buf_ld32(make_rsrc(beta + row_of(c), valid_rows(c) * 4),
+                                          (16 * wave + l16) * (uint32_t)H * 4));
     };
     auto v_rsrc = [&](int64_t c) {
         return make_rsrc(v + row_of(c) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)));
@@ -521,41 +544,49 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         // over the position groups then supplies the product of the groups
         // before (pre) and after (post) this lane's, and the tile total.
         const int pb = (int)p0;
-        float e1[RP][CPL], e2[RP][CPL], fB[CPL], dec[CPL], pre[CPL], post[CPL];
+        const QKRes rq_next = qk_rsrc(c + 1);
+        float al[RP][CPL], dec[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
-            float al[RP];
 #pragma unroll
-            for (int r = 0; r < RP; ++r) al[r] = fexp2(la_r[r][cc] * kLog2e);
-            float p = 1.f;
+            for (int r = 0; r < RP; ++r) al[r][cc] = fexp2(la_r[r][cc] * kLog2e);
+            float t = al[0][cc];
 #pragma unroll
-            for (int r = 0; r < RP; ++r) { p *= al[r]; e1[r][cc] = p; }
-            float sfx = 1.f;
-#pragma unroll
-            for (int r = RP - 1; r >= 0; --r) { e2[r][cc] = sfx; sfx *= al[r]; }
-            dec[cc] = p;
-            pre[cc] = 1.f;
-            post[cc] = 1.f;
+            for (int r = 1; r < RP; ++r) t *= al[r][cc];
+            dec[cc] = t;                       // product over this lane's positions
         }
         load_la(c + 1);
         __builtin_amdgcn_sched_barrier(0);
-        // Butterfly over the position groups (block of LPR lanes, then 2 LPR, ...).
+        // Butterfly over the position groups (blocks of LPR lanes, then 2 LPR,
+        // ...): pre = product of the groups before this lane's, post = of the
+        // groups after it, dec = of all (the same value in every lane).
+        float pre[CPL], post[CPL];
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) { pre[cc] = 1.f; post[cc] = 1.f; }
         auto level = [&](auto dtag) {
             constexpr int D = decltype(dtag)::value;
+            const bool upper = (lane & D) != 0;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
-                const float other = xor_lanes<D>(dec[cc]);   // product of the partner block
-                if (lane & D) pre[cc] *= other; else post[cc] *= other;
-                dec[cc] *= other;                            // same value in both blocks
+                const LoHi b = block_pair<D>(dec[cc]);
+                pre[cc] *= upper ? b.lo : 1.f;
+                post[cc] *= upper ? 1.f : b.hi;
+                dec[cc] = b.lo * b.hi;
             }
         };
         if constexpr (LPR == 8) level(std::integral_constant<int, 8>{});
         level(std::integral_constant<int, 16>{});
         level(std::integral_constant<int, 32>{});
+        // Running products seeded with pre and post.
+        float e1[RP][CPL], e2[RP][CPL], fB[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
+            float p = pre[cc];
 #pragma unroll
-            for (int r = 0; r < RP; ++r) { e1[r][cc] *= pre[cc]; e2[r][cc] *= post[cc]; }
+            for (int r = 0; r < RP; ++r) { p *= al[r][cc]; e1[r][cc] = p; }
+            float sfx = post[cc];
+#pragma unroll
+            for (int r = RP - 1; r >= 0; --r) { e2[r][cc] = sfx; if (r > 0) sfx *= al[r][cc]; }
             fB[cc] = __builtin_amdgcn_rcpf(dec[cc]);
         }
         if (pg == 0) {
@@ -581,8 +612,12 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             OP::put8(sKE1 + orow, ke1[0], ke1[1]);
             OP::put8(sKE2 + (pb + r) * PL::LDK2 + cb, ke2[0], ke2[1]);
             OP::put8(sKB + orow, kb[0], kb[1]);
+            // Row r of q and k is consumed: load the same row of the next chunk.
+            load_qk_row(rq_next, r);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (lane < 16) sBS[ti * 16 + lane] = beta_r;
+        load_beta(c + 1);
         wave_lds_sync();
 
         // P and M of the tile, transposed (D[s][r] = sum_c Kb[s][c] X[r][c]):
@@ -608,8 +643,6 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             }
             OP::put4(sPD + (ti * 16 + l16) * PL::LD16 + 4 * lg, vp);
         }
-        load_qk(c + 1);
-        __builtin_amdgcn_sched_barrier(0);
         wave_lds_sync();
 
         // A = (I + Diag(b) M)^{-1} Diag(b) by right-looking substitution on
@@ -668,7 +701,16 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             using Seg = typename OP::Seg;
             // All LDS operands of this tile, issued together.
             Seg kseg[NCT], qseg[NCT], eseg[NCT];
-            f32x4 dec[NCT];
+            // Tile decay of the state rows 16 ct + 4 lg + e: the 4 NCT values a
+            // 16-lane row needs are spread over its lanes (VPL each) and
+            // broadcast into the multiplies.
+            constexpr int VPL = NCT / 4;
+            float decv[VPL];
+            {
+                const float* dp = sDEC + i * DK + 16 * ((VPL * l16) >> 2) + 4 * lg + ((VPL * l16) & 3);
+#pragma unroll
+                for (int u = 0; u < VPL; ++u) decv[u] = dp[u];
+            }
             const OT* krow = sKE1 + (16 * i + l16) * PL::LDK;
             const OT* qrow = sQE1 + (16 * i + l16) * PL::LDK;
 #pragma unroll
@@ -680,7 +722,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 eseg[ct] = OP::seg_t(sKE2 + 16 * i * PL::LDK2 + 16 * ct, tro, PL::LDK2);
-                dec[ct] = *reinterpret_cast<const f32x4*>(sDEC + i * DK + 16 * ct + 4 * lg);
+
             }
             Xop Sop[NCT];
 #pragma unroll
@@ -708,7 +750,12 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             oacc = OP::acc_seg16_k32(Wop, pseg, oacc);
             // S <- Diag(2^X) S + (K e2)^T W   (lane v = l16, rows c = 16 ct + 4 lg + e)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Sacc[ct] = OP::seg_acc16(eseg[ct], Wop, Sacc[ct] * dec[ct]);
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4 sd4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sd4[e] = Sacc[ct][e] * row_bcast(decv[(4 * ct + e) % VPL], (4 * ct + e) / VPL);
+                Sacc[ct] = OP::seg_acc16(eseg[ct], Wop, sd4);
+            }
             const uint32_t ooff = ((16 * i + l16) * (uint32_t)H * DV + 4 * lg) * (uint32_t)sizeof(T);
             if constexpr (sizeof(T) == 2) buf_st64(OP::cvt(oacc), ro, ooff);
             else buf_st128(__builtin_bit_cast(u32x4, oacc), ro, ooff);
@@ -721,7 +768,12 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     if (wave < kSIW) {
         if (nchunks > 0) {
             load_la(0);
-            load_qk(0);
+            {
+                const QKRes r0 = qk_rsrc(0);
+#pragma unroll
+                for (int r = 0; r < RP; ++r) load_qk_row(r0, r);
+                load_beta(0);
+            }
             si(0);
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
@@ -730,6 +782,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             }
         }
     } else {
+        // The state-dependent waves carry the serial chain of the recurrence:
+        // they take issue priority over the producer waves on their SIMD.
+        __builtin_amdgcn_s_setprio(2);
         // This wave's state slab: Sacc[ct][e] = S[16 ct + 4 lg + e][vcol + l16].
         f32x4 Sacc[NCT];
         const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
