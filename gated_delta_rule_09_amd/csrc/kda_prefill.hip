@@ -383,13 +383,14 @@ struct Plan {
     static constexpr int PD = KE2 + kC * LDK2 * ES;                // [4][16][LD16] P per tile
     static constexpr int AD = PD + kTiles * 16 * LD16 * ES;        // [4][16][LD16] A per tile
     static constexpr int DEC = AD + kTiles * 16 * LD16 * ES;       // [4][DK] fp32 2^X per tile
-    static constexpr int BUF = DEC + kTiles * DK * 4;
+    static constexpr int MSTR = 20;                                // fp32 stride of M^T rows (16-byte aligned)
+    static constexpr int MS = DEC + kTiles * DK * 4;               // [4][16][MSTR] fp32 M^T per tile
+    static constexpr int BS = MS + kTiles * 16 * MSTR * 4;         // [4][16] fp32 beta per tile
+    static constexpr int BUF = BS + kTiles * 16 * 4;
     // scratch
     static constexpr int KB = 2 * BUF;                             // [C][LDK]   k * 2^{-x}
-    static constexpr int MSTR = 20;                                // fp32 stride of M^T rows (16-byte aligned)
-    static constexpr int MS = KB + kC * LDK * ES;                  // [4][16][MSTR] fp32 M^T per tile
-    static constexpr int BS = MS + kTiles * 16 * MSTR * 4;         // [4][16] fp32 beta per tile
-    static constexpr int TOTAL = BS + kTiles * 16 * 4;
+    static constexpr int FLAG = KB + kC * LDK * ES;                // [4] int: chunk whose A of tile i is ready
+    static constexpr int TOTAL = FLAG + 16;
     static_assert(BUF % 16 == 0 && KB % 16 == 0, "alignment");
     static_assert(TOTAL <= 160 * 1024, "LDS plan exceeds 160 KB");
 };
@@ -432,8 +433,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     const int h = unit - n * H;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float* sMS = reinterpret_cast<float*>(smem + PL::MS);
-    float* sBS = reinterpret_cast<float*>(smem + PL::BS);
+    int* sFLAG = reinterpret_cast<int*>(smem + PL::FLAG);
     OT* sKB = reinterpret_cast<OT*>(smem + PL::KB);
 
     const int tid = threadIdx.x;
@@ -534,8 +534,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         OT* sKE1 = reinterpret_cast<OT*>(buf + PL::KE1);
         OT* sKE2 = reinterpret_cast<OT*>(buf + PL::KE2);
         OT* sPD = reinterpret_cast<OT*>(buf + PL::PD);
-        OT* sAD = reinterpret_cast<OT*>(buf + PL::AD);
         float* sDEC = reinterpret_cast<float*>(buf + PL::DEC);
+        float* sMS = reinterpret_cast<float*>(buf + PL::MS);
+        float* sBS = reinterpret_cast<float*>(buf + PL::BS);
         const int ti = wave;
         // Lane = (key channels cb .. cb+7; tile positions pb .. pb+RP-1).
         // alpha = 2^{l2}; e1 = prefix products over the tile, e2 = suffix
@@ -643,8 +644,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             }
             OP::put4(sPD + (ti * 16 + l16) * PL::LD16 + 4 * lg, vp);
         }
-        wave_lds_sync();
+    };
 
+    // ---- Inverse of tile ti of chunk c (run by the state-dependent waves, one
+    // tile each, on the M and beta the producer waves left in buffer c & 1).
+    auto inverse = [&](int64_t c, int ti) {
+        unsigned char* buf = smem + (c & 1) * PL::BUF;
+        OT* sAD = reinterpret_cast<OT*>(buf + PL::AD);
+        const float* sMS = reinterpret_cast<const float*>(buf + PL::MS);
+        const float* sBS = reinterpret_cast<const float*>(buf + PL::BS);
         // A = (I + Diag(b) M)^{-1} Diag(b) by right-looking substitution on
         // all 64 lanes: lane = (column j = lane / 4, row residue q = lane % 4)
         // and holds rows r = 4 m + q, m = 0..3, of column j of X = (I +
@@ -683,6 +691,20 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
 #pragma unroll
             for (int m = 0; m < 4; ++m) OP::put(sAD + (ti * 16 + 4 * m + q) * PL::LD16 + j, xs[m] * bj);
         }
+        // Publish: every write of A is complete before the flag names chunk c.
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(sFLAG + ti, (int)c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    // Wait until the A of tile i of chunk c is published.  Each flag is written
+    // by a wave whose own path up to that write has no waits, so the loop
+    // ends; the bound only guards against a logic error.
+    auto wait_a = [&](int64_t c, int i) {
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(sFLAG + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == (int)c) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
     // ---- SD: state-dependent part of chunk c from buffer (c & 1).  Wave w = value columns.
@@ -696,9 +718,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         const OT* sAD = reinterpret_cast<const OT*>(buf + PL::AD);
         const float* sDEC = reinterpret_cast<const float*>(buf + PL::DEC);
         const Rsrc ro = make_rsrc(o + row_of(c) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)));
+        inverse(c, wave - kSIW);
 #pragma unroll
         for (int i = 0; i < kTiles; ++i) {
             using Seg = typename OP::Seg;
+            if (i != wave - kSIW) wait_a(c, i);
             // All LDS operands of this tile, issued together.
             Seg kseg[NCT], qseg[NCT], eseg[NCT];
             // Tile decay of the state rows 16 ct + 4 lg + e: the 4 NCT values a
@@ -793,6 +817,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     #pragma unroll
             for (int e = 0; e < 4; ++e)
                 Sacc[ct][e] = init_state ? init_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] : 0.f;
+        if (wave == kSIW && lane < kTiles) __hip_atomic_store(sFLAG + lane, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (nchunks > 0) {
             {
                 const Rsrc rv0 = v_rsrc(0);
