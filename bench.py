@@ -97,6 +97,18 @@ def kernel_digest(kernel: str) -> str:
     return h.hexdigest()
 
 
+def measured_util(kernel: str):
+    """rocprofv3 MfmaUtil / VALUBusy (percent) recorded for the kernel's current code, or None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("code_digest") != kernel_digest(kernel):
+        return None, None
+    return rec.get("mfma_util_pct"), rec.get("valu_busy_pct")
+
+
 def measured_traffic(kernel: str, launch_ms: float):
     """HBM bytes per launch measured by the rocprofv3 FETCH_SIZE / WRITE_SIZE
     passes (calibrated against a plain copy), as GB/s over this run's launch
@@ -208,7 +220,9 @@ def main():
                      "traffic": measured_traffic("prefill", pre_ms),
                      "kernel": "prefill_kernel", "avg_launch_ms": round(pre_ms, 4),
                      "algorithmic_bytes_per_launch": pre_bytes,
-                     "mfma_frac_algorithmic": round(pre_tflops / BF16_DENSE_PEAK_TFLOPS, 4)},
+                     "mfma_frac_algorithmic": round(pre_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+                     "mfma_util_rocprof_pct": measured_util("prefill")[0],
+                     "valu_busy_rocprof_pct": measured_util("prefill")[1]},
         "decode": {"gbps": round(dec_gbps, 1), "ms_per_step": round(dec_ms, 4),
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                                 "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
