@@ -52,6 +52,51 @@ def test_long_64k_workload_four_heads():
     run_and_check(x, "bf16", heads=heads, what="long 64K, log alpha ~ U[-5,-3]")
 
 
+@pytest.mark.timeout(900)
+def test_long_1m_capacity_four_heads(tmp_path):
+    """Capacity run: one sequence of 1,048,576 tokens, H=96, d=128 (about 155 GB of device
+    memory), checked against the fp64 oracle on 4 sampled heads.  The oracle heads run as
+    four child processes (about 90 s each on one core); progress is printed while waiting."""
+    import subprocess
+    import sys
+    import time
+    x = ki.workload_inputs("long_1m", device=device())
+    announce("prefill capacity run T=1,048,576 H=96 d=128 bf16 (log alpha ~ U[-5,-3])")
+    o, fin = kda_chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state, None)
+    torch.cuda.synchronize()
+    heads = sorted(np.random.default_rng(5).choice(96, 4, replace=False).tolist())
+    procs, dirs = [], []
+    worker = str(__import__("pathlib").Path(__file__).with_name("oracle_worker.py"))
+    for h in heads:
+        d = tmp_path / f"head{h}"
+        d.mkdir()
+        for name, t in (("q", x.q), ("k", x.k), ("v", x.v), ("log_alpha", x.log_alpha)):
+            np.save(d / f"{name}.npy", host(t[:, h:h + 1]))
+        np.save(d / "beta.npy", host(x.beta[:, h:h + 1]))
+        np.save(d / "init_state.npy", host(x.init_state[:, h:h + 1]))
+        np.save(d / "o_gpu.npy", host(o[:, h:h + 1]))
+        np.save(d / "final_gpu.npy", host(fin[:, h:h + 1]))
+        dirs.append(d)
+    del x, o, fin
+    torch.cuda.empty_cache()
+    env = dict(__import__("os").environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1")
+    for d in dirs:
+        procs.append(subprocess.Popen([sys.executable, worker, str(d)], env=env))
+    t0 = time.time()
+    while any(p.poll() is None for p in procs):
+        time.sleep(15)
+        announce(f"  oracle heads {heads}: {sum(p.poll() is not None for p in procs)}/4 done after {time.time() - t0:.0f} s")
+    assert all(p.returncode == 0 for p in procs), [p.returncode for p in procs]
+    worst_o = worst_f = 0.0
+    for h, d in zip(heads, dirs):
+        eo = rel_err(np.load(d / "o_gpu.npy"), np.load(d / "o_ref.npy"))
+        ef = rel_err(np.load(d / "final_gpu.npy"), np.load(d / "final_ref.npy"))
+        announce(f"  head {h}: rel err o={eo:.3e} final={ef:.3e}")
+        worst_o, worst_f = max(worst_o, eo), max(worst_f, ef)
+    assert worst_o <= TOL["bf16"], worst_o
+    assert worst_f <= TOL["bf16"], worst_f
+
+
 @pytest.mark.parametrize("lengths", [[1], [37], [100], [64], [65], [128 + 17], [1, 1, 1], [5, 0, 70, 1, 33]])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ragged_lengths(lengths, dtype):
