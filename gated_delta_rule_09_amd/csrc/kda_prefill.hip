@@ -719,35 +719,43 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         const float* sDEC = reinterpret_cast<const float*>(buf + PL::DEC);
         const Rsrc ro = make_rsrc(o + row_of(c) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)));
         inverse(c, wave - kSIW);
-#pragma unroll
-        for (int i = 0; i < kTiles; ++i) {
-            using Seg = typename OP::Seg;
-            if (i != wave - kSIW) wait_a(c, i);
-            // All LDS operands of this tile, issued together.
-            Seg kseg[NCT], qseg[NCT], eseg[NCT];
-            // Tile decay of the state rows 16 ct + 4 lg + e: the 4 NCT values a
-            // 16-lane row needs are spread over its lanes (VPL each) and
-            // broadcast into the multiplies.
-            constexpr int VPL = NCT / 4;
-            float decv[VPL];
-            {
-                const float* dp = sDEC + i * DK + 16 * ((VPL * l16) >> 2) + 4 * lg + ((VPL * l16) & 3);
-#pragma unroll
-                for (int u = 0; u < VPL; ++u) decv[u] = dp[u];
-            }
+        // LDS operands of one tile (A excepted: it is read after its flag).
+        // Tile decay of the state rows 16 ct + 4 lg + e: the 4 NCT values a
+        // 16-lane row needs are spread over its lanes (VPL each) and broadcast
+        // into the multiplies.
+        using Seg = typename OP::Seg;
+        constexpr int VPL = NCT / 4;
+        struct TileOps { Seg kseg[NCT], qseg[NCT], eseg[NCT], pseg; float decv[VPL]; };
+        auto load_ops = [&](int i, TileOps& t) {
             const OT* krow = sKE1 + (16 * i + l16) * PL::LDK;
             const OT* qrow = sQE1 + (16 * i + l16) * PL::LDK;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) kseg[ct] = OP::seg(krow + 16 * ct);
+            for (int ct = 0; ct < NCT; ++ct) t.kseg[ct] = OP::seg(krow + 16 * ct);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) t.qseg[ct] = OP::seg(qrow + 16 * ct);
+            t.pseg = OP::seg(sPD + (16 * i + l16) * PL::LD16);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) t.eseg[ct] = OP::seg_t(sKE2 + 16 * i * PL::LDK2 + 16 * ct, tro, PL::LDK2);
+            const float* dp = sDEC + i * DK + 16 * ((VPL * l16) >> 2) + 4 * lg + ((VPL * l16) & 3);
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) t.decv[u] = dp[u];
+        };
+        // Software pipeline over the tiles: the operands of tile i + 1 are read
+        // while tile i computes.  A of tile i is read first (after its flag), so
+        // that waiting for it never waits for the prefetch (LDS returns in order).
+        TileOps ops[2];
+        load_ops(0, ops[0]);
+#pragma unroll
+        for (int i = 0; i < kTiles; ++i) {
+            if (i != wave - kSIW) wait_a(c, i);
             const Seg aseg = OP::seg(sAD + (16 * i + l16) * PL::LD16);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) qseg[ct] = OP::seg(qrow + 16 * ct);
-            const Seg pseg = OP::seg(sPD + (16 * i + l16) * PL::LD16);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                eseg[ct] = OP::seg_t(sKE2 + 16 * i * PL::LDK2 + 16 * ct, tro, PL::LDK2);
-
-            }
+            if (i + 1 < kTiles) load_ops(i + 1, ops[(i + 1) & 1]);
+            const TileOps& cur = ops[i & 1];
+            const auto& kseg = cur.kseg;
+            const auto& qseg = cur.qseg;
+            const auto& eseg = cur.eseg;
+            const Seg pseg = cur.pseg;
+            const auto& decv = cur.decv;
             Xop Sop[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) Sop[ct] = OP::cvt(Sacc[ct]);
