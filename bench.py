@@ -34,6 +34,9 @@ N_DECODE = 512
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * D * 2 + D * 4 + 4 + D * 2          # 1540
 STATE_BYTES = D * D * 4                                                  # 64 KiB
 DECODE_BYTES_PER_PAIR = 2 * STATE_BYTES + 3 * D * 2 + D * 4 + 4 + D * 2  # 132,612
+# Gated entry points: bf16 decay logits replace fp32 log-decay, fp32 beta logits replace beta.
+GATED_PREFILL_BYTES_PER_TOKEN_HEAD = 3 * D * 2 + D * 2 + 4 + D * 2        # 1284
+GATED_DECODE_BYTES_PER_PAIR = 2 * STATE_BYTES + 3 * D * 2 + D * 2 + 4 + D * 2
 # Algorithmic flops per token-head, chunk 64, causal triangles only.
 PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 2 * 64 * (D + D)              # 131,072
 
@@ -124,12 +127,57 @@ def measured_traffic(kernel: str, launch_ms: float):
     return round((rec["hbm_bytes_read"] + rec["hbm_bytes_written"]) / (launch_ms * 1e-3) / 1e9, 1)
 
 
+def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
+    """The gated entry points (decay / write-strength logits mapped in-kernel) on the
+    same 64K prefill and 512 x 96 decode shapes, timed outside the headline step."""
+    import torch
+    xg = ki.gated_inputs([T_PREFILL], H=H, d=D, dtype="bf16", seed=3, device=dev)
+    og = torch.empty_like(xg.v)
+    fg = torch.empty_like(xg.init_state)
+    w = ki.DECODE_WORKLOAD
+    sg = ki.decode_state(w["N"], w["H"], w["d"], seed=w["seed"], device=dev)
+    dg = ki.decode_gated_inputs(w["N"], w["H"], w["d"], dtype=w["dtype"], seed=w["seed"], step=0, device=dev)
+    odg = torch.empty_like(dg["v"])
+
+    def run_prefill():
+        prefill_gated(xg.q, xg.k, xg.v, xg.g_logits, xg.a_log, xg.beta_logits, xg.init_state, None, o=og,
+                      final_state=fg)
+
+    def run_decode():
+        decode_gated(dg["q"], dg["k"], dg["v"], dg["g_logits"], dg["a_log"], dg["beta_logits"], sg, o=odg)
+
+    def timed(fn, reps):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    pre_ms = timed(run_prefill, max(1, args.steps))
+    dec_ms = timed(run_decode, max(1, args.steps))
+    pre_bytes = T_PREFILL * H * GATED_PREFILL_BYTES_PER_TOKEN_HEAD + 2 * H * STATE_BYTES
+    dec_bytes = N_DECODE * H * GATED_DECODE_BYTES_PER_PAIR
+    return {"prefill_ms": round(pre_ms, 4), "prefill_tokens_per_s": round(T_PREFILL / (pre_ms * 1e-3), 1),
+            "prefill_gbps": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+            "prefill_bytes_per_token_head": GATED_PREFILL_BYTES_PER_TOKEN_HEAD,
+            "decode_ms": round(dec_ms, 4), "decode_gbps": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+            "decode_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "config": "gated entry points: bf16 decay logits z ~ N(0, 4), A_h ~ U[-1, 1], fp32 beta logits "
+                      "~ N(0, 1); same shapes as the headline step"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gated", action="store_true", help="skip the timing of the gated entry points")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -140,7 +188,8 @@ def main():
 
     import torch
     import kda_inputs as ki
-    from gated_delta_rule_09_amd import kda_chunk_prefill, kda_decode_step
+    from gated_delta_rule_09_amd import (kda_chunk_prefill, kda_chunk_prefill_gated, kda_decode_step,
+                                         kda_decode_step_gated)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -229,6 +278,8 @@ def main():
                                 "traffic": measured_traffic("decode", dec_ms),
                                 "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec_bytes}},
     }
+    if not args.no_gated:
+        res["gated"] = time_gated(args, dev, stream, ki, kda_chunk_prefill_gated, kda_decode_step_gated)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)

@@ -36,6 +36,11 @@ SIGNATURES = {
                                           _VP, _VP, _VP]),
     "kda_decode_step": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP,
                                         _I32, _I32, _I32, _I32, ctypes.c_int, _VP, _VP]),
+    "kda_chunk_prefill_gated": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
+                                                _VP, _VP, _VP]),
+    "kda_decode_step_gated": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                              _I32, _I32, _I32, _I32, ctypes.c_int, _VP, _VP]),
 }
 
 _lib = None
@@ -67,7 +72,7 @@ def load(path: Optional[str] = None):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.kda_abi_version() != 1:
+    if lib.kda_abi_version() != 2:
         raise RuntimeError("libkda ABI version mismatch")
     if path is None:
         _lib = lib
@@ -163,4 +168,73 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              N, H, d_k, d_v, code, _ptr(o), _stream_handle(dev))
     if st != KDA_OK:
         raise KDAError("kda_decode_step", st)
+    return o
+
+
+def kda_chunk_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            g_logits: torch.Tensor, a_log: torch.Tensor, beta_logits: torch.Tensor,
+                            init_state: Optional[torch.Tensor] = None,
+                            cu_seqlens: Optional[torch.Tensor] = None,
+                            o: Optional[torch.Tensor] = None,
+                            final_state: Optional[torch.Tensor] = None,
+                            output_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill from decay / write-strength logits (see include/kda.h,
+    kda_chunk_prefill_gated).  Returns (o, final_state)."""
+    lib = load()
+    T, H, d_k = q.shape
+    d_v = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(k, "k", (T, H, d_k), dt, dev)
+    _check(v, "v", (T, H, d_v), dt, dev)
+    _check(g_logits, "g_logits", (T, H, d_k), dt, dev)
+    _check(a_log, "a_log", (H,), torch.float32, dev)
+    _check(beta_logits, "beta_logits", (T, H), torch.float32, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (N, H, d_k, d_v), torch.float32, dev)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((T, H, d_v), dtype=dt, device=dev)
+    _check(o, "o", (T, H, d_v), dt, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, d_k, d_v), torch.float32, dev)
+    st = lib.kda_chunk_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(a_log), _ptr(beta_logits),
+                                     _ptr(init_state), _ptr(cu_seqlens), N, T, H, d_k, d_v, code,
+                                     _ptr(o), _ptr(final_state), _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_chunk_prefill_gated", st)
+    return o, final_state
+
+
+def kda_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          g_logits: torch.Tensor, a_log: torch.Tensor, beta_logits: torch.Tensor,
+                          state: torch.Tensor, o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One KDA decode step from decay / write-strength logits; ``state`` is updated
+    in place.  Returns o [N, H, d_v]."""
+    lib = load()
+    N, H, d_k = q.shape
+    d_v = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(q, "q", (N, H, d_k), dt, dev)
+    _check(k, "k", (N, H, d_k), dt, dev)
+    _check(v, "v", (N, H, d_v), dt, dev)
+    _check(g_logits, "g_logits", (N, H, d_k), dt, dev)
+    _check(a_log, "a_log", (H,), torch.float32, dev)
+    _check(beta_logits, "beta_logits", (N, H), torch.float32, dev)
+    _check(state, "state", (N, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, d_v), dtype=dt, device=dev)
+    _check(o, "o", (N, H, d_v), dt, dev)
+    st = lib.kda_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(a_log), _ptr(beta_logits),
+                                   _ptr(state), N, H, d_k, d_v, code, _ptr(o), _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_decode_step_gated", st)
     return o

@@ -72,29 +72,80 @@ const char* kda_status_string(kda_status s) {
 
 const char* kda_last_error(void) { return g_last_error; }
 
+}  // extern "C"
+
+namespace {
+
+kda_status decode_impl(const char* name, const void* q, const void* k, const void* v, const void* decay,
+                       const float* beta, const float* a_log, bool gated, float* state, int32_t N, int32_t H,
+                       int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, void* stream) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (N < 0 || H < 1 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !decay || !beta || !state || !o || (gated && !a_log)) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(decay) ||
+        !aligned16(beta) || !aligned16(state) || !aligned16(o) || (gated && !aligned16(a_log)))
+        return KDA_ERR_ALIGN;
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    kda::DecodeArgs a{q, k, v, decay, beta, state, o, N, H, d_k, d_v,
+                      dtype == KDA_BF16, reinterpret_cast<hipStream_t>(stream), gated, a_log};
+    hipError_t e = kda::launch_decode(a);
+    if (e != hipSuccess) {
+        set_error(name, e);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+kda_status prefill_impl(const char* name, const void* q, const void* k, const void* v, const void* decay,
+                        const float* beta, const float* a_log, bool gated, const float* init_state,
+                        const int32_t* cu_seqlens, int32_t N, int64_t total_T, int32_t H, int32_t d_k,
+                        int32_t d_v, kda_dtype dtype, void* o, float* final_state, void* stream) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (N < 1 || H < 1 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
+    if (dtype == KDA_F32 && d_k != 64) return KDA_ERR_SHAPE;
+    if (cu_seqlens == nullptr && N != 1) return KDA_ERR_SHAPE;
+    if (N > 65535 || H > 65535) return KDA_ERR_SHAPE;   // grid dimensions
+    if ((int64_t)N * H > (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
+    if (total_T > 0 && (!q || !k || !v || !decay || !beta || !o || (gated && !a_log))) return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, decay, beta, a_log, init_state, cu_seqlens, o, final_state};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    if (total_T == 0 && final_state == nullptr) return KDA_OK;
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    kda::PrefillArgs a{q, k, v, decay, beta, init_state, cu_seqlens, N, total_T, H, d_k, d_v,
+                       dtype == KDA_BF16, o, final_state, reinterpret_cast<hipStream_t>(stream), gated, a_log};
+    hipError_t e = kda::launch_prefill(a);
+    if (e != hipSuccess) {
+        set_error(name, e);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta,
                            float* state, int32_t N, int32_t H,
                            int32_t d_k, int32_t d_v, kda_dtype dtype,
                            void* o, void* stream) {
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
-    if (N < 0 || H < 1 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
-    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
-    if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
-        !aligned16(beta) || !aligned16(state) || !aligned16(o))
-        return KDA_ERR_ALIGN;
-    kda_status st = check_device();
-    if (st != KDA_OK) return st;
-    kda::DecodeArgs a{q, k, v, log_alpha, beta, state, o, N, H, d_k, d_v,
-                      dtype == KDA_BF16, reinterpret_cast<hipStream_t>(stream)};
-    hipError_t e = kda::launch_decode(a);
-    if (e != hipSuccess) {
-        set_error("kda_decode_step launch", e);
-        return KDA_ERR_HIP;
-    }
-    return KDA_OK;
+    return decode_impl("kda_decode_step launch", q, k, v, log_alpha, beta, nullptr, false, state, N, H, d_k, d_v,
+                       dtype, o, stream);
+}
+
+kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
+                                 const void* g_logits, const float* a_log, const float* beta_logits,
+                                 float* state, int32_t N, int32_t H,
+                                 int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                 void* o, void* stream) {
+    return decode_impl("kda_decode_step_gated launch", q, k, v, g_logits, beta_logits, a_log, true, state, N, H,
+                       d_k, d_v, dtype, o, stream);
 }
 
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v,
@@ -103,27 +154,18 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v,
                              int32_t N, int64_t total_T, int32_t H,
                              int32_t d_k, int32_t d_v, kda_dtype dtype,
                              void* o, float* final_state, void* stream) {
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
-    if (N < 1 || H < 1 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
-    if (dtype == KDA_F32 && d_k != 64) return KDA_ERR_SHAPE;
-    if (cu_seqlens == nullptr && N != 1) return KDA_ERR_SHAPE;
-    if (N > 65535 || H > 65535) return KDA_ERR_SHAPE;   // grid dimensions
-    if ((int64_t)N * H > (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
-    if (total_T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
-    const void* ptrs[] = {q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
-    if (total_T == 0 && final_state == nullptr) return KDA_OK;
-    kda_status st = check_device();
-    if (st != KDA_OK) return st;
-    kda::PrefillArgs a{q, k, v, log_alpha, beta, init_state, cu_seqlens, N, total_T, H, d_k, d_v,
-                       dtype == KDA_BF16, o, final_state, reinterpret_cast<hipStream_t>(stream)};
-    hipError_t e = kda::launch_prefill(a);
-    if (e != hipSuccess) {
-        set_error("kda_chunk_prefill launch", e);
-        return KDA_ERR_HIP;
-    }
-    return KDA_OK;
+    return prefill_impl("kda_chunk_prefill launch", q, k, v, log_alpha, beta, nullptr, false, init_state,
+                        cu_seqlens, N, total_T, H, d_k, d_v, dtype, o, final_state, stream);
+}
+
+kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v,
+                                   const void* g_logits, const float* a_log, const float* beta_logits,
+                                   const float* init_state, const int32_t* cu_seqlens,
+                                   int32_t N, int64_t total_T, int32_t H,
+                                   int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                   void* o, float* final_state, void* stream) {
+    return prefill_impl("kda_chunk_prefill_gated launch", q, k, v, g_logits, beta_logits, a_log, true, init_state,
+                        cu_seqlens, N, total_T, H, d_k, d_v, dtype, o, final_state, stream);
 }
 
 }  // extern "C"

@@ -27,11 +27,16 @@ namespace kda {
 
 constexpr int kDecodeThreads = 1024;
 
-template <typename T, int DK, int DV>
+// GATED: `decay` holds decay logits z (element type T) and `beta` the
+// write-strength logits; the lower-bounded map of section 1.2 of the notes
+// (Kimi K3 row of its table), log alpha = -5 Sigmoid(e^{A_h} z) and
+// beta = Sigmoid(logit), is applied on the fly.  Otherwise `decay` holds fp32
+// log alpha and `beta` beta.
+template <typename T, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    float* __restrict__ state, T* __restrict__ o, int64_t pairs) {
+    const void* __restrict__ decay, const float* __restrict__ beta, const float* __restrict__ a_log,
+    float* __restrict__ state, T* __restrict__ o, int32_t H, int64_t pairs) {
     constexpr int NT = kDecodeThreads;
     constexpr int QUADS = DV / 4;          // threads per state row
     constexpr int RG = NT / QUADS;         // row groups
@@ -62,7 +67,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // Per-channel vectors.
     float kq_part = 0.f;
     if (t < DK) {
-        const float a = __expf(log_alpha[pair * DK + t]);
+        float a;
+        if constexpr (GATED) {
+            const float u = __expf(a_log[pair % H]) * Elem<T>::load(reinterpret_cast<const T*>(decay), pair * DK + t);
+            a = __expf(-5.f / (1.f + __expf(-u)));
+        } else {
+            a = __expf(reinterpret_cast<const float*>(decay)[pair * DK + t]);
+        }
         const float kk = Elem<T>::load(k, pair * DK + t);
         const float qq = Elem<T>::load(q, pair * DK + t);
         s_a[t] = a;
@@ -98,7 +109,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         float kq = 0.f;
 #pragma unroll
         for (int i = 0; i < NT / kWave; ++i) kq += s_kq[i];
-        const float w = beta[pair] * (Elem<T>::load(v, pair * DV + t) - es);
+        const float b = GATED ? 1.f / (1.f + __expf(-beta[pair])) : beta[pair];
+        const float w = b * (Elem<T>::load(v, pair * DV + t) - es);
         s_w[t] = w;
         Elem<T>::store(o, pair * DV + t, os + w * kq);
     }
@@ -117,9 +129,14 @@ template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     const int64_t pairs = (int64_t)a.N * a.H;
     if (pairs == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)pairs), dim3(kDecodeThreads), 0, a.stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.state,
-                       (T*)a.o, pairs);
+    if (a.gated)
+        hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3((unsigned)pairs), dim3(kDecodeThreads), 0,
+                           a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.a_log,
+                           a.state, (T*)a.o, a.H, pairs);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3((unsigned)pairs), dim3(kDecodeThreads), 0,
+                           a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.a_log,
+                           a.state, (T*)a.o, a.H, pairs);
     return hipGetLastError();
 }
 

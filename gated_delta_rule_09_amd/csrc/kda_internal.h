@@ -6,23 +6,31 @@
 
 namespace kda {
 
+// With `gated` set, `log_alpha` points at decay logits z in the element type
+// of q (bf16 or fp32), `beta` at fp32 write-strength logits, and `a_log` at
+// the per-head log-scales A_h [H]; the kernels apply the lower-bounded map
+// g = -5 Sigmoid(e^{A_h} z), beta = Sigmoid(logit) on the fly.
 struct DecodeArgs {
     const void* q; const void* k; const void* v;
-    const float* log_alpha; const float* beta;
+    const void* log_alpha; const float* beta;
     float* state; void* o;
     int32_t N, H, d_k, d_v;
     bool bf16;
     hipStream_t stream;
+    bool gated = false;
+    const float* a_log = nullptr;
 };
 
 struct PrefillArgs {
     const void* q; const void* k; const void* v;
-    const float* log_alpha; const float* beta;
+    const void* log_alpha; const float* beta;
     const float* init_state; const int32_t* cu_seqlens;
     int32_t N; int64_t total_T; int32_t H, d_k, d_v;
     bool bf16;
     void* o; float* final_state;
     hipStream_t stream;
+    bool gated = false;
+    const float* a_log = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

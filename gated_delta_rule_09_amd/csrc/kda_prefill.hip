@@ -395,12 +395,20 @@ struct Plan {
     static_assert(TOTAL <= 160 * 1024, "LDS plan exceeds 160 KB");
 };
 
-template <typename T, int DK, int DV>
+// GATED: `decay` holds the decay logits z (element type T) and `beta` the
+// write-strength logits; the lower-bounded map of section 1.2 of the notes
+// (Kimi K3 row of its table), g = -5 Sigmoid(e^{A_h} z), beta = Sigmoid(logit),
+// is applied on the fly.  Otherwise `decay` holds log alpha (fp32) and `beta`
+// beta.
+template <typename T, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const void* __restrict__ decay, const float* __restrict__ beta, const float* __restrict__ a_log,
     const float* __restrict__ init_state, const int32_t* __restrict__ cu_seqlens,
     int64_t total_T, int H, int units, T* __restrict__ o, float* __restrict__ final_state) {
+    // Decay input: fp32 log alpha, or decay logits of type T (GATED).
+    using DT = typename std::conditional<GATED, T, float>::type;
+    const DT* log_alpha = reinterpret_cast<const DT*>(decay);
     using OT = T;
     using OP = Op<OT>;
     using PL = Plan<OT, DK>;
@@ -431,6 +439,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     if (unit >= units) return;
     const int n = unit / H;
     const int h = unit - n * H;
+    const float eA = GATED ? __expf(a_log[h]) : 1.f;    // e^{A_h}, the per-head logit scale
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     int* sFLAG = reinterpret_cast<int*>(smem + PL::FLAG);
@@ -461,7 +470,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     // descriptors whose range ends after the chunk's last valid token, so rows
     // past a sequence's end read as zero (decay 1, key, query, value and beta
     // 0) and output rows past it are not written.
-    float la_r[RP][CPL];
+    constexpr int LAW = CPL * (int)sizeof(DT) / 4;   // 32-bit words holding CPL decay inputs
+    uint32_t la_w[RP][LAW];      // raw words: fp32 log alpha, or decay logits (GATED)
     uint32_t qw_r[RP][QWN], kw_r[RP][QWN];
     float beta_r;
     uint32_t v_r[kTiles][4];     // v[16 i + 4 lg + e][vcol + l16], raw words
@@ -480,16 +490,16 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     // as its registers are free: log-decay after the exponentials, q, k and
     // beta after the products of the tile.
     auto load_la = [&](int64_t c) {
-        const Rsrc rla = make_rsrc(log_alpha + row_of(c) * DK, valid_rows(c) * (DK * 4));
+        const Rsrc rla = make_rsrc(log_alpha + row_of(c) * DK, valid_rows(c) * (DK * (uint32_t)sizeof(DT)));
         const uint32_t rs = (uint32_t)H * DK;
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
             const uint32_t el = (p0 + r) * rs + cb;
 #pragma unroll
-            for (int u = 0; u < CPL / 4; ++u) {
-                const u32x4 a = buf_ld128(rla, el * 4 + 16 * u);
+            for (int u = 0; u < LAW / 4; ++u) {
+                const u32x4 a = buf_ld128(rla, el * (uint32_t)sizeof(DT) + 16 * u);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) la_r[r][4 * u + j] = __uint_as_float(a[j]);
+                for (int j = 0; j < 4; ++j) la_w[r][4 * u + j] = a[j];
             }
         }
     };
@@ -547,10 +557,34 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         const int pb = (int)p0;
         const QKRes rq_next = qk_rsrc(c + 1);
         float al[RP][CPL], dec[CPL];
+        // Base-2 log-decay of each element.  GATED: g = -5 Sigmoid(e^{A_h} z);
+        // rows past the end of a partial chunk get g = 0 (their logits read
+        // as 0, which the map does not send to 0).
+        float l2[RP][CPL];
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                if constexpr (GATED) {
+                    const float u = eA * lane_elem<T>(la_w[r], cc);
+                    l2[r][cc] = (-5.f * kLog2e) * __builtin_amdgcn_rcpf(1.f + fexp2(-kLog2e * u));
+                } else {
+                    l2[r][cc] = __uint_as_float(la_w[r][cc]) * kLog2e;
+                }
+            }
+        if constexpr (GATED) {
+            const int lc = chunk_len(c);
+            if (lc < kC) {
+#pragma unroll
+                for (int r = 0; r < RP; ++r)
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc) l2[r][cc] = (int)p0 + r < lc ? l2[r][cc] : 0.f;
+            }
+        }
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
 #pragma unroll
-            for (int r = 0; r < RP; ++r) al[r][cc] = fexp2(la_r[r][cc] * kLog2e);
+            for (int r = 0; r < RP; ++r) al[r][cc] = fexp2(l2[r][cc]);
             float t = al[0][cc];
 #pragma unroll
             for (int r = 1; r < RP; ++r) t *= al[r][cc];
@@ -617,7 +651,13 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             load_qk_row(rq_next, r);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (lane < 16) sBS[ti * 16 + lane] = beta_r;
+        if (lane < 16) {
+            if constexpr (GATED)   // beta = Sigmoid(logit); 0 past the end of the sequence
+                sBS[ti * 16 + lane] = 16 * ti + lane < chunk_len(c)
+                                          ? __builtin_amdgcn_rcpf(1.f + fexp2(-kLog2e * beta_r)) : 0.f;
+            else
+                sBS[ti * 16 + lane] = beta_r;
+        }
         load_beta(c + 1);
         wave_lds_sync();
 
@@ -848,10 +888,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     }
 }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool GATED>
 hipError_t launch_t(const PrefillArgs& a) {
     using PL = Plan<T, DK>;
-    auto kern = prefill_kernel<T, DK, DV>;
+    auto kern = prefill_kernel<T, DK, DV, GATED>;
     static bool attr_set = false;   // per instantiation; the attribute is a property of the function
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -863,20 +903,26 @@ hipError_t launch_t(const PrefillArgs& a) {
     constexpr int NV = DV / kBV;
     const int64_t blocks = NV == 2 ? 16 * ((units + 7) / 8) : units;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kNW), PL::TOTAL, a.stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.init_state,
-                       a.cu_seqlens, a.total_T, a.H, (int)units, (T*)a.o, a.final_state);
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.a_log,
+                       a.init_state, a.cu_seqlens, a.total_T, a.H, (int)units, (T*)a.o, a.final_state);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a) {
+template <bool GATED>
+hipError_t launch_prefill_g(const PrefillArgs& a) {
     if (a.bf16) {
-        if (a.d_k == 128) return a.d_v == 128 ? launch_t<uint16_t, 128, 128>(a) : launch_t<uint16_t, 128, 64>(a);
-        return a.d_v == 128 ? launch_t<uint16_t, 64, 128>(a) : launch_t<uint16_t, 64, 64>(a);
+        if (a.d_k == 128)
+            return a.d_v == 128 ? launch_t<uint16_t, 128, 128, GATED>(a) : launch_t<uint16_t, 128, 64, GATED>(a);
+        return a.d_v == 128 ? launch_t<uint16_t, 64, 128, GATED>(a) : launch_t<uint16_t, 64, 64, GATED>(a);
     }
     // fp32 operands: d_k = 64 only (the LDS plan of d_k = 128 would exceed 160 KB).
-    return a.d_v == 128 ? launch_t<float, 64, 128>(a) : launch_t<float, 64, 64>(a);
+    return a.d_v == 128 ? launch_t<float, 64, 128, GATED>(a) : launch_t<float, 64, 64, GATED>(a);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a) {
+    return a.gated ? launch_prefill_g<true>(a) : launch_prefill_g<false>(a);
 }
 
 }  // namespace kda

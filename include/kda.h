@@ -70,7 +70,7 @@ typedef enum {
 } kda_dtype;
 
 /* Version of this interface; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 int kda_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -134,6 +134,40 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            float* state, int32_t N, int32_t H,
                            int32_t d_k, int32_t d_v, kda_dtype dtype,
                            void* o, void* stream);
+
+/*
+ * Gated variants: the decay and the write strength are given as logits and
+ * mapped inside the kernels by the lower-bounded decay of section 1.2 of the
+ * notes (the Kimi K3 row of its table of decay mappings):
+ *
+ *     log_alpha = g_min * Sigmoid(exp(A_h) * z),   g_min = -5,
+ *     beta      = Sigmoid(b),
+ *
+ * so log_alpha lies in (-5, 0) by construction and the section-1.2 bound needs
+ * no precondition.  A_h is the per-head log-scale of that section; z and b are
+ * the outputs of the decay and write-strength projections, which stay outside
+ * this library.  Everything else (layouts, ownership, asynchrony, errors,
+ * shapes) is as for the ungated calls; the extra arguments are
+ *
+ *   g_logits    : [T, H, d_k] decay logits z, element type given by `dtype`
+ *                 (bf16 halves the bytes of the fp32 log_alpha input).
+ *   a_log       : [H] float32, A_h per head (16-byte aligned; required).
+ *   beta_logits : [T, H] float32 write-strength logits b.
+ *
+ * For decode, T is replaced by N.
+ */
+kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v,
+                                   const void* g_logits, const float* a_log, const float* beta_logits,
+                                   const float* init_state, const int32_t* cu_seqlens,
+                                   int32_t N, int64_t total_T, int32_t H,
+                                   int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                   void* o, float* final_state, void* stream);
+
+kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
+                                 const void* g_logits, const float* a_log, const float* beta_logits,
+                                 float* state, int32_t N, int32_t H,
+                                 int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                 void* o, void* stream);
 
 #ifdef __cplusplus
 }

@@ -182,3 +182,55 @@ def to_numpy(x: Optional[torch.Tensor]):
     if x.dtype == torch.bfloat16:
         x = x.float()
     return x.numpy()
+
+
+# ---- logit inputs of the gated entry points ---------------------------------
+# Recipe: q, k, v and the initial state as above; decay logits z ~ N(0, 2^2)
+# in the element type of q (a wide spread, so that g = -5 Sigmoid(e^A z) spans
+# nearly all of (-5, 0)); per-head log-scales A_h ~ U[-1, 1]; write-strength
+# logits b ~ N(0, 1) in fp32 (Sigmoid(b) has the law of beta above).
+
+@dataclass
+class GatedInputs:
+    q: torch.Tensor            # [T, H, d_k]  dtype
+    k: torch.Tensor            # [T, H, d_k]  dtype
+    v: torch.Tensor            # [T, H, d_v]  dtype
+    g_logits: torch.Tensor     # [T, H, d_k]  dtype
+    a_log: torch.Tensor        # [H]          fp32
+    beta_logits: torch.Tensor  # [T, H]       fp32
+    init_state: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+    lengths: list
+
+
+def gated_inputs(lengths: Sequence[int], H: int, d: int, dtype: str = "bf16", init: str = "normal",
+                 seed: int = 0, device="cpu", d_v: Optional[int] = None, packed: Optional[bool] = None,
+                 slab: int = 65536) -> GatedInputs:
+    """Draw one packed prefill batch for the gated entry points (recipe above)."""
+    base = prefill_inputs(lengths, H, d, dtype=dtype, la_law="zero", init=init, seed=seed, device=device,
+                          d_v=d_v, packed=packed, slab=slab)
+    T = int(sum(int(x) for x in lengths))
+    dt = torch_dtype(dtype)
+    g = _generator(seed * 7 + 101, device)
+    z = torch.empty((T, H, d), dtype=dt, device=device)
+    b = torch.empty((T, H), dtype=torch.float32, device=device)
+    for t0 in range(0, T, slab):
+        t1 = min(T, t0 + slab)
+        z[t0:t1] = (2.0 * torch.randn((t1 - t0, H, d), generator=g, device=device)).to(dt)
+        b[t0:t1] = torch.randn((t1 - t0, H), generator=g, device=device)
+    a = 2.0 * torch.rand((H,), generator=g, device=device) - 1.0
+    return GatedInputs(base.q, base.k, base.v, z, a, b, base.init_state, base.cu_seqlens, base.lengths)
+
+
+def decode_gated_inputs(N: int, H: int, d: int, dtype: str = "bf16", seed: int = 4, step: int = 0,
+                        device="cpu", d_v: Optional[int] = None) -> dict:
+    """Per-step decode inputs of the gated entry point: q, k, v, g_logits, beta_logits
+    (recipe above); a_log is drawn from ``seed`` alone, so it is the same every step."""
+    base = decode_inputs(N, H, d, dtype=dtype, la_law="zero", seed=seed, step=step, device=device, d_v=d_v)
+    dt = torch_dtype(dtype)
+    g = _generator(seed * 1_000_033 + 104729 * (step + 1), device)
+    z = (2.0 * torch.randn((N, H, d), generator=g, device=device)).to(dt)
+    b = torch.randn((N, H), generator=g, device=device)
+    ga = _generator(seed * 7 + 101, device)
+    a = 2.0 * torch.rand((H,), generator=ga, device=device) - 1.0
+    return dict(q=base["q"], k=base["k"], v=base["v"], g_logits=z, a_log=a, beta_logits=b)

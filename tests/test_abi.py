@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for s in range(7):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -76,6 +76,36 @@ def test_decode_rejects_bad_arguments_before_touching_the_device(kw, code):
     assert decode(L.load(), **kw) == code
 
 
+def prefill_gated(lib, **kw):
+    a = dict(q=P, k=P, v=P, z=P, A=P, b=P, init=None, cu=None, N=1, T=64, H=2, dk=64, dv=64, dt=L.KDA_BF16,
+             o=P, fin=P)
+    a.update(kw)
+    return lib.kda_chunk_prefill_gated(a["q"], a["k"], a["v"], a["z"], a["A"], a["b"], a["init"], a["cu"], a["N"],
+                                       a["T"], a["H"], a["dk"], a["dv"], a["dt"], a["o"], a["fin"], None)
+
+
+def decode_gated(lib, **kw):
+    a = dict(q=P, k=P, v=P, z=P, A=P, b=P, S=P, N=4, H=2, dk=64, dv=64, dt=L.KDA_BF16, o=P)
+    a.update(kw)
+    return lib.kda_decode_step_gated(a["q"], a["k"], a["v"], a["z"], a["A"], a["b"], a["S"], a["N"], a["H"],
+                                     a["dk"], a["dv"], a["dt"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), 3), (dict(dk=96), 2), (dict(N=2), 2), (dict(dt=L.KDA_F32, dk=128), 2),
+    (dict(z=None), 1), (dict(A=None), 1), (dict(b=None), 1), (dict(A=MIS), 4), (dict(z=MIS), 4),
+])
+def test_gated_prefill_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert prefill_gated(L.load(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=-1), 3), (dict(dk=32), 2), (dict(A=None), 1), (dict(z=None), 1), (dict(A=MIS), 4),
+])
+def test_gated_decode_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert decode_gated(L.load(), **kw) == code
+
+
 def test_empty_calls_are_no_ops():
     lib = L.load()
     assert decode(lib, N=0, q=None, S=None) == 0
@@ -94,6 +124,8 @@ def _has_gpu():
 def test_valid_call_without_a_device_reports_no_device():
     assert prefill(L.load()) == 5
     assert decode(L.load()) == 5
+    assert prefill_gated(L.load()) == 5
+    assert decode_gated(L.load()) == 5
 
 
 def test_binding_raises_when_library_missing(tmp_path):
