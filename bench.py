@@ -10,7 +10,9 @@ Inputs are synthetic, seeded, and resident in device memory before timing.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Prints one JSON line.  `value` is prefill tokens/s; decode state-update
-bandwidth is reported under "decode".  Kernel durations come from HIP events
+bandwidth is reported under "decode"; the gated entry points and the output
+epilogue (standalone, after the gated prefill, fused into the gated decode)
+are timed after the headline step under "gated" and "epilogue".  Kernel durations come from HIP events
 recorded on the stream the kernels are launched on.
 """
 
@@ -37,6 +39,10 @@ DECODE_BYTES_PER_PAIR = 2 * STATE_BYTES + 3 * D * 2 + D * 4 + 4 + D * 2  # 132,6
 # Gated entry points: bf16 decay logits replace fp32 log-decay, fp32 beta logits replace beta.
 GATED_PREFILL_BYTES_PER_TOKEN_HEAD = 3 * D * 2 + D * 2 + 4 + D * 2        # 1284
 GATED_DECODE_BYTES_PER_PAIR = 2 * STATE_BYTES + 3 * D * 2 + D * 2 + 4 + D * 2
+# Output epilogue: read o and the gate logits, write y (bf16); the gain is d_v fp32 per launch.
+EPILOGUE_BYTES_PER_TOKEN_HEAD = 3 * D * 2                                # 768
+# Gated decode with the epilogue fused: the gate logits are read, y replaces o.
+EPILOGUE_DECODE_BYTES_PER_PAIR = GATED_DECODE_BYTES_PER_PAIR + D * 2
 # Algorithmic flops per token-head, chunk 64, causal triangles only.
 PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 2 * 64 * (D + D)              # 131,072
 
@@ -81,6 +87,8 @@ KERNEL_SOURCES = {
                 "gated_delta_rule_09_amd/csrc/kda_internal.h"],
     "decode": ["gated_delta_rule_09_amd/csrc/kda_decode.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
                "gated_delta_rule_09_amd/csrc/kda_internal.h"],
+    "epilogue": ["gated_delta_rule_09_amd/csrc/kda_epilogue.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
+                 "gated_delta_rule_09_amd/csrc/kda_internal.h"],
 }
 
 
@@ -127,6 +135,64 @@ def measured_traffic(kernel: str, launch_ms: float):
     return round((rec["hbm_bytes_read"] + rec["hbm_bytes_written"]) / (launch_ms * 1e-3) / 1e9, 1)
 
 
+def _timed(args, stream, fn, reps):
+    """Average duration of fn() over reps back-to-back calls, HIP events on `stream`."""
+    import torch
+    for _ in range(max(1, args.warmup)):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_epilogue(args, dev, stream, ki, lib):
+    """The output epilogue (Sigmoid(W_g x) * RMSNorm(o), head-wise): the standalone
+    kernel on the 64K x 96-head output, the gated prefill followed by it, and the
+    gated decode with it fused, timed outside the headline step."""
+    import torch
+    e = ki.epilogue_inputs((T_PREFILL, H, D), "bf16", seed=64, device=dev)
+    y = torch.empty_like(e["o"])
+    epi_ms = _timed(args, stream, lambda: lib.kda_output_gate_rmsnorm(e["o"], e["gate"], e["weight"], y=y),
+                    max(1, args.steps))
+    epi_bytes = T_PREFILL * H * EPILOGUE_BYTES_PER_TOKEN_HEAD + D * 4
+    del y
+    xg = ki.gated_inputs([T_PREFILL], H=H, d=D, dtype="bf16", seed=3, device=dev)
+    yp = torch.empty_like(xg.v)
+    fg = torch.empty_like(xg.init_state)
+    pre_ms = _timed(args, stream, lambda: lib.kda_chunk_prefill_gated_epilogue(
+        xg.q, xg.k, xg.v, xg.g_logits, xg.a_log, xg.beta_logits, e["gate"], e["weight"],
+        init_state=xg.init_state, y=yp, final_state=fg), max(1, args.steps))
+    del xg, yp, fg, e
+    w = ki.DECODE_WORKLOAD
+    sg = ki.decode_state(w["N"], w["H"], w["d"], seed=w["seed"], device=dev)
+    dg = ki.decode_gated_inputs(w["N"], w["H"], w["d"], dtype=w["dtype"], seed=w["seed"], step=0, device=dev)
+    og = ki.out_gate_inputs((w["N"], w["H"], w["d"]), "bf16", seed=w["seed"], device=dev)
+    yd = torch.empty_like(dg["v"])
+    dec_ms = _timed(args, stream, lambda: lib.kda_decode_step_gated_epilogue(
+        dg["q"], dg["k"], dg["v"], dg["g_logits"], dg["a_log"], dg["beta_logits"], og["gate"], sg,
+        norm_weight=og["weight"], y=yd), max(1, args.steps))
+    dec_bytes = N_DECODE * H * EPILOGUE_DECODE_BYTES_PER_PAIR
+    epi_gbps = epi_bytes / (epi_ms * 1e-3) / 1e9
+    return {"standalone": {"ms": round(epi_ms, 4), "gbps": round(epi_gbps, 1),
+                           "frac": round(epi_gbps / HBM_PEAK_GBPS, 4),
+                           "traffic": measured_traffic("epilogue", epi_ms),
+                           "bytes_per_token_head": EPILOGUE_BYTES_PER_TOKEN_HEAD,
+                           "kernel": "gate_rmsnorm_kernel", "rows": T_PREFILL * H},
+            "prefill_gated_epilogue": {"ms": round(pre_ms, 4),
+                                       "tokens_per_s": round(T_PREFILL / (pre_ms * 1e-3), 1)},
+            "decode_gated_epilogue": {"ms": round(dec_ms, 4),
+                                      "gbps": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                                      "frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "config": "y = Sigmoid(g) * w * o / sqrt(mean(o^2) + 1e-5) per (token, head); o ~ N(0, 1) x "
+                      "10^U[-3, 1] per row, g ~ N(0, 4), w ~ U[0.5, 1.5]; 64K x 96 x 128 bf16 and the "
+                      "512 x 96 gated decode"}
+
+
 def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
     """The gated entry points (decay / write-strength logits mapped in-kernel) on the
     same 64K prefill and 512 x 96 decode shapes, timed outside the headline step."""
@@ -146,20 +212,8 @@ def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
     def run_decode():
         decode_gated(dg["q"], dg["k"], dg["v"], dg["g_logits"], dg["a_log"], dg["beta_logits"], sg, o=odg)
 
-    def timed(fn, reps):
-        for _ in range(max(1, args.warmup)):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
-
-    pre_ms = timed(run_prefill, max(1, args.steps))
-    dec_ms = timed(run_decode, max(1, args.steps))
+    pre_ms = _timed(args, stream, run_prefill, max(1, args.steps))
+    dec_ms = _timed(args, stream, run_decode, max(1, args.steps))
     pre_bytes = T_PREFILL * H * GATED_PREFILL_BYTES_PER_TOKEN_HEAD + 2 * H * STATE_BYTES
     dec_bytes = N_DECODE * H * GATED_DECODE_BYTES_PER_PAIR
     return {"prefill_ms": round(pre_ms, 4), "prefill_tokens_per_s": round(T_PREFILL / (pre_ms * 1e-3), 1),
@@ -178,6 +232,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gated", action="store_true", help="skip the timing of the gated entry points")
+    ap.add_argument("--no-epilogue", action="store_true", help="skip the timing of the output epilogue")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -280,6 +335,11 @@ def main():
     }
     if not args.no_gated:
         res["gated"] = time_gated(args, dev, stream, ki, kda_chunk_prefill_gated, kda_decode_step_gated)
+    if not args.no_epilogue:
+        del x, o, fin, state, dx, od
+        torch.cuda.empty_cache()
+        import gated_delta_rule_09_amd as lib
+        res["epilogue"] = time_epilogue(args, dev, stream, ki, lib)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)

@@ -1,10 +1,13 @@
-"""MI355X (gfx950) Kimi Delta Attention: chunkwise prefill and decode.
+"""MI355X (gfx950) Kimi Delta Attention: chunkwise prefill, decode and the
+output epilogue.
 
 The computation lives in libkda.so (hand-written HIP kernels behind the C ABI
 of include/kda.h).  This package only marshals torch tensors into that ABI.
 """
-from ._lib import (KDAError, kda_chunk_prefill, kda_chunk_prefill_gated, kda_decode_step,
-                   kda_decode_step_gated, load)
+from ._lib import (RMS_EPS, KDAError, kda_chunk_prefill, kda_chunk_prefill_gated,
+                   kda_chunk_prefill_gated_epilogue, kda_decode_step, kda_decode_step_gated,
+                   kda_decode_step_gated_epilogue, kda_output_gate_rmsnorm, load)
 
 __all__ = ["kda_chunk_prefill", "kda_decode_step", "kda_chunk_prefill_gated", "kda_decode_step_gated",
-           "load", "KDAError"]
+           "kda_output_gate_rmsnorm", "kda_chunk_prefill_gated_epilogue", "kda_decode_step_gated_epilogue",
+           "RMS_EPS", "load", "KDAError"]

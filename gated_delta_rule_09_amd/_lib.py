@@ -23,10 +23,12 @@ KDA_OK = 0
 KDA_F32 = 0
 KDA_BF16 = 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
-           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_NO_DEVICE", 6: "KDA_ERR_HIP"}
+           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_NO_DEVICE", 6: "KDA_ERR_HIP", 7: "KDA_ERR_VALUE"}
+ABI_VERSION = 3
+RMS_EPS = 1e-5      # epsilon of the model's RMSNorm
 
 # Every symbol include/kda.h declares, with its ctypes signature.
-_VP, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+_VP, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 SIGNATURES = {
     "kda_abi_version": (ctypes.c_int, []),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -41,6 +43,12 @@ SIGNATURES = {
                                                 _VP, _VP, _VP]),
     "kda_decode_step_gated": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                               _I32, _I32, _I32, _I32, ctypes.c_int, _VP, _VP]),
+    "kda_output_gate_rmsnorm": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _F32, ctypes.c_int, _VP, _VP]),
+    "kda_chunk_prefill_gated_epilogue": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP, _VP,
+                                                         _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
+                                                         _VP, _VP, _VP]),
+    "kda_decode_step_gated_epilogue": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP,
+                                                       _I32, _I32, _I32, _I32, ctypes.c_int, _VP, _VP]),
 }
 
 _lib = None
@@ -72,7 +80,7 @@ def load(path: Optional[str] = None):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.kda_abi_version() != 2:
+    if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError("libkda ABI version mismatch")
     if path is None:
         _lib = lib
@@ -238,3 +246,111 @@ def kda_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != KDA_OK:
         raise KDAError("kda_decode_step_gated", st)
     return o
+
+
+def _check_epilogue_args(out_gate: torch.Tensor, norm_weight: Optional[torch.Tensor], shape, dt, dev):
+    _check(out_gate, "out_gate_logits", shape, dt, dev)
+    if norm_weight is not None:
+        _check(norm_weight, "norm_weight", (shape[-1],), torch.float32, dev)
+
+
+def kda_output_gate_rmsnorm(o: torch.Tensor, gate_logits: torch.Tensor,
+                            norm_weight: Optional[torch.Tensor] = None, eps: float = RMS_EPS,
+                            y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Output epilogue y = Sigmoid(gate_logits) * w * o / sqrt(mean(o^2) + eps) over
+    the last axis (see include/kda.h).  ``y`` may be ``o`` or ``gate_logits``."""
+    lib = load()
+    dev, dt = o.device, o.dtype
+    code = _dtype_code(dt)
+    if o.dim() < 1:
+        raise ValueError("o must have a channel axis")
+    d_v = o.shape[-1]
+    _check(o, "o", o.shape, dt, dev)
+    _check_epilogue_args(gate_logits, norm_weight, o.shape, dt, dev)
+    if y is None:
+        y = torch.empty_like(o)
+    _check(y, "y", o.shape, dt, dev)
+    rows = o.numel() // d_v if d_v else 0
+    st = lib.kda_output_gate_rmsnorm(_ptr(o), _ptr(gate_logits), _ptr(norm_weight), rows, d_v, float(eps), code,
+                                     _ptr(y), _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_output_gate_rmsnorm", st)
+    return y
+
+
+def kda_chunk_prefill_gated_epilogue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                     g_logits: torch.Tensor, a_log: torch.Tensor, beta_logits: torch.Tensor,
+                                     out_gate_logits: torch.Tensor, norm_weight: Optional[torch.Tensor] = None,
+                                     eps: float = RMS_EPS,
+                                     init_state: Optional[torch.Tensor] = None,
+                                     cu_seqlens: Optional[torch.Tensor] = None,
+                                     y: Optional[torch.Tensor] = None,
+                                     final_state: Optional[torch.Tensor] = None,
+                                     output_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated chunkwise prefill followed by the output epilogue (see include/kda.h,
+    kda_chunk_prefill_gated_epilogue).  Returns (y, final_state)."""
+    lib = load()
+    T, H, d_k = q.shape
+    d_v = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(k, "k", (T, H, d_k), dt, dev)
+    _check(v, "v", (T, H, d_v), dt, dev)
+    _check(g_logits, "g_logits", (T, H, d_k), dt, dev)
+    _check(a_log, "a_log", (H,), torch.float32, dev)
+    _check(beta_logits, "beta_logits", (T, H), torch.float32, dev)
+    _check_epilogue_args(out_gate_logits, norm_weight, (T, H, d_v), dt, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (N, H, d_k, d_v), torch.float32, dev)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if y is None:
+        y = torch.empty((T, H, d_v), dtype=dt, device=dev)
+    _check(y, "y", (T, H, d_v), dt, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, d_k, d_v), torch.float32, dev)
+    st = lib.kda_chunk_prefill_gated_epilogue(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(a_log),
+                                              _ptr(beta_logits), _ptr(out_gate_logits), _ptr(norm_weight),
+                                              float(eps), _ptr(init_state), _ptr(cu_seqlens), N, T, H, d_k, d_v,
+                                              code, _ptr(y), _ptr(final_state), _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_chunk_prefill_gated_epilogue", st)
+    return y, final_state
+
+
+def kda_decode_step_gated_epilogue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   g_logits: torch.Tensor, a_log: torch.Tensor, beta_logits: torch.Tensor,
+                                   out_gate_logits: torch.Tensor, state: torch.Tensor,
+                                   norm_weight: Optional[torch.Tensor] = None, eps: float = RMS_EPS,
+                                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One gated decode step with the output epilogue fused; ``state`` is updated
+    in place.  Returns y [N, H, d_v]."""
+    lib = load()
+    N, H, d_k = q.shape
+    d_v = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(q, "q", (N, H, d_k), dt, dev)
+    _check(k, "k", (N, H, d_k), dt, dev)
+    _check(v, "v", (N, H, d_v), dt, dev)
+    _check(g_logits, "g_logits", (N, H, d_k), dt, dev)
+    _check(a_log, "a_log", (H,), torch.float32, dev)
+    _check(beta_logits, "beta_logits", (N, H), torch.float32, dev)
+    _check_epilogue_args(out_gate_logits, norm_weight, (N, H, d_v), dt, dev)
+    _check(state, "state", (N, H, d_k, d_v), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, d_v), dtype=dt, device=dev)
+    _check(y, "y", (N, H, d_v), dt, dev)
+    st = lib.kda_decode_step_gated_epilogue(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(a_log),
+                                            _ptr(beta_logits), _ptr(out_gate_logits), _ptr(norm_weight),
+                                            float(eps), _ptr(state), N, H, d_k, d_v, code, _ptr(y),
+                                            _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_decode_step_gated_epilogue", st)
+    return y

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <math.h>
 #include <string.h>
 
 #include <mutex>
@@ -66,6 +67,7 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_ALIGN: return "pointer not 16-byte aligned";
         case KDA_ERR_NO_DEVICE: return "no usable gfx950 HIP device";
         case KDA_ERR_HIP: return "HIP runtime error";
+        case KDA_ERR_VALUE: return "an argument value is out of range";
     }
     return "unknown status";
 }
@@ -76,21 +78,30 @@ const char* kda_last_error(void) { return g_last_error; }
 
 namespace {
 
+bool valid_eps(float eps) { return isfinite(eps) && eps >= 0.f; }
+
+// `out_gate` non-null selects the fused output epilogue (gated decode only).
 kda_status decode_impl(const char* name, const void* q, const void* k, const void* v, const void* decay,
                        const float* beta, const float* a_log, bool gated, float* state, int32_t N, int32_t H,
-                       int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, void* stream) {
+                       int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, void* stream,
+                       bool epilogue = false, const void* out_gate = nullptr, const float* norm_weight = nullptr,
+                       float eps = 0.f) {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (N < 0 || H < 1 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
     if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (epilogue && !valid_eps(eps)) return KDA_ERR_VALUE;
     if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !decay || !beta || !state || !o || (gated && !a_log)) return KDA_ERR_NULL;
+    if (!q || !k || !v || !decay || !beta || !state || !o || (gated && !a_log) || (epilogue && !out_gate))
+        return KDA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(decay) ||
-        !aligned16(beta) || !aligned16(state) || !aligned16(o) || (gated && !aligned16(a_log)))
+        !aligned16(beta) || !aligned16(state) || !aligned16(o) || (gated && !aligned16(a_log)) ||
+        (epilogue && !aligned16(out_gate)) || (norm_weight && !aligned16(norm_weight)))
         return KDA_ERR_ALIGN;
     kda_status st = check_device();
     if (st != KDA_OK) return st;
     kda::DecodeArgs a{q, k, v, decay, beta, state, o, N, H, d_k, d_v,
-                      dtype == KDA_BF16, reinterpret_cast<hipStream_t>(stream), gated, a_log};
+                      dtype == KDA_BF16, reinterpret_cast<hipStream_t>(stream), gated, a_log,
+                      epilogue ? out_gate : nullptr, norm_weight, eps};
     hipError_t e = kda::launch_decode(a);
     if (e != hipSuccess) {
         set_error(name, e);
@@ -119,6 +130,29 @@ kda_status prefill_impl(const char* name, const void* q, const void* k, const vo
     kda::PrefillArgs a{q, k, v, decay, beta, init_state, cu_seqlens, N, total_T, H, d_k, d_v,
                        dtype == KDA_BF16, o, final_state, reinterpret_cast<hipStream_t>(stream), gated, a_log};
     hipError_t e = kda::launch_prefill(a);
+    if (e != hipSuccess) {
+        set_error(name, e);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+kda_status epilogue_checks(const void* o, const void* gate, const float* weight, int64_t rows, int32_t d_v,
+                           float eps, kda_dtype dtype, const void* y) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (rows < 0 || rows > kda::epilogue_max_rows() || !supported_d(d_v)) return KDA_ERR_SHAPE;
+    if (!valid_eps(eps)) return KDA_ERR_VALUE;
+    if (rows == 0) return KDA_OK;
+    if (!o || !gate || !y) return KDA_ERR_NULL;
+    if (!aligned16(o) || !aligned16(gate) || !aligned16(y) || (weight && !aligned16(weight))) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+kda_status epilogue_launch(const char* name, const void* o, const void* gate, const float* weight, int64_t rows,
+                           int32_t d_v, float eps, kda_dtype dtype, void* y, void* stream) {
+    kda::EpilogueArgs a{o, gate, weight, rows, d_v, eps, dtype == KDA_BF16, y,
+                        reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = kda::launch_epilogue(a);
     if (e != hipSuccess) {
         set_error(name, e);
         return KDA_ERR_HIP;
@@ -166,6 +200,47 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v,
                                    void* o, float* final_state, void* stream) {
     return prefill_impl("kda_chunk_prefill_gated launch", q, k, v, g_logits, beta_logits, a_log, true, init_state,
                         cu_seqlens, N, total_T, H, d_k, d_v, dtype, o, final_state, stream);
+}
+
+kda_status kda_output_gate_rmsnorm(const void* o, const void* gate_logits, const float* norm_weight,
+                                   int64_t rows, int32_t d_v, float eps, kda_dtype dtype,
+                                   void* y, void* stream) {
+    kda_status st = epilogue_checks(o, gate_logits, norm_weight, rows, d_v, eps, dtype, y);
+    if (st != KDA_OK || rows == 0) return st;
+    st = check_device();
+    if (st != KDA_OK) return st;
+    return epilogue_launch("kda_output_gate_rmsnorm launch", o, gate_logits, norm_weight, rows, d_v, eps, dtype, y,
+                           stream);
+}
+
+kda_status kda_chunk_prefill_gated_epilogue(const void* q, const void* k, const void* v,
+                                            const void* g_logits, const float* a_log, const float* beta_logits,
+                                            const void* out_gate_logits, const float* norm_weight, float eps,
+                                            const float* init_state, const int32_t* cu_seqlens,
+                                            int32_t N, int64_t total_T, int32_t H,
+                                            int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                            void* y, float* final_state, void* stream) {
+    // Everything is validated before the first launch, so a rejected call
+    // leaves y and final_state untouched.
+    if (total_T < 0 || H < 1 || total_T > INT64_MAX / H) return KDA_ERR_SHAPE;
+    const int64_t rows = total_T * H;
+    kda_status st = epilogue_checks(y, out_gate_logits, norm_weight, rows, d_v, eps, dtype, y);
+    if (st != KDA_OK) return st;
+    st = prefill_impl("kda_chunk_prefill_gated_epilogue launch", q, k, v, g_logits, beta_logits, a_log, true,
+                      init_state, cu_seqlens, N, total_T, H, d_k, d_v, dtype, y, final_state, stream);
+    if (st != KDA_OK || rows == 0) return st;
+    return epilogue_launch("kda_chunk_prefill_gated_epilogue launch", y, out_gate_logits, norm_weight, rows, d_v,
+                           eps, dtype, y, stream);
+}
+
+kda_status kda_decode_step_gated_epilogue(const void* q, const void* k, const void* v,
+                                          const void* g_logits, const float* a_log, const float* beta_logits,
+                                          const void* out_gate_logits, const float* norm_weight, float eps,
+                                          float* state, int32_t N, int32_t H,
+                                          int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                          void* y, void* stream) {
+    return decode_impl("kda_decode_step_gated_epilogue launch", q, k, v, g_logits, beta_logits, a_log, true, state,
+                       N, H, d_k, d_v, dtype, y, stream, true, out_gate_logits, norm_weight, eps);
 }
 
 }  // extern "C"

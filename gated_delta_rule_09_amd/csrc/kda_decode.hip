@@ -32,11 +32,16 @@ constexpr int kDecodeThreads = 1024;
 // (Kimi K3 row of its table), log alpha = -5 Sigmoid(e^{A_h} z) and
 // beta = Sigmoid(logit), is applied on the fly.  Otherwise `decay` holds fp32
 // log alpha and `beta` beta.
-template <typename T, int DK, int DV, bool GATED>
+// NORM: the output epilogue of section 1.3 is applied before the store,
+// y = Sigmoid(og) * nw * o / sqrt(mean(o^2) + eps) over the pair's d_v
+// channels (nw null: gain 1); the pair's whole o lives in this workgroup, so
+// it costs one more reduction and no extra pass.
+template <typename T, int DK, int DV, bool GATED, bool NORM>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const void* __restrict__ decay, const float* __restrict__ beta, const float* __restrict__ a_log,
-    float* __restrict__ state, T* __restrict__ o, int32_t H, int64_t pairs) {
+    float* __restrict__ state, T* __restrict__ o, int32_t H, int64_t pairs,
+    const T* __restrict__ og, const float* __restrict__ nw, float eps) {
     constexpr int NT = kDecodeThreads;
     constexpr int QUADS = DV / 4;          // threads per state row
     constexpr int RG = NT / QUADS;         // row groups
@@ -47,6 +52,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __shared__ f32x4 s_red[2][RG][QUADS];
     __shared__ float s_w[DV];
     __shared__ float s_kq[NT / kWave];
+    __shared__ float s_ss[DV / kWave];
 
     const int64_t pair = blockIdx.x;
     if (pair >= pairs) return;
@@ -98,6 +104,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     s_red[1][rg][vq] = op;
     __syncthreads();
 
+    float out = 0.f;
     if (t < DV) {
         const int cq = t / 4, cl = t % 4;
         float es = 0.f, os = 0.f;
@@ -112,9 +119,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         const float b = GATED ? 1.f / (1.f + __expf(-beta[pair])) : beta[pair];
         const float w = b * (Elem<T>::load(v, pair * DV + t) - es);
         s_w[t] = w;
-        Elem<T>::store(o, pair * DV + t, os + w * kq);
+        out = os + w * kq;
+        if constexpr (NORM) {
+            const float ss = wave_sum(out * out);      // DV is a multiple of the wave size
+            if ((t % kWave) == 0) s_ss[t / kWave] = ss;
+        } else {
+            Elem<T>::store(o, pair * DV + t, out);
+        }
     }
     __syncthreads();
+
+    if constexpr (NORM) {
+        if (t < DV) {
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < DV / kWave; ++i) ss += s_ss[i];
+            const float gate = 1.f / (1.f + __expf(-Elem<T>::load(og, pair * DV + t)));
+            const float gain = nw ? nw[t] : 1.f;
+            Elem<T>::store(o, pair * DV + t, out * rsqrtf(ss * (1.f / DV) + eps) * gain * gate);
+        }
+    }
 
     const f32x4 w4 = {s_w[4 * vq], s_w[4 * vq + 1], s_w[4 * vq + 2], s_w[4 * vq + 3]};
 #pragma unroll
@@ -125,18 +149,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
 }
 
+template <typename T, int DK, int DV, bool GATED, bool NORM>
+static void launch_decode_v(const DecodeArgs& a, int64_t pairs) {
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV, GATED, NORM>), dim3((unsigned)pairs), dim3(kDecodeThreads), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.a_log,
+                       a.state, (T*)a.o, a.H, pairs, (const T*)a.out_gate, a.norm_weight, a.eps);
+}
+
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     const int64_t pairs = (int64_t)a.N * a.H;
     if (pairs == 0) return hipSuccess;
-    if (a.gated)
-        hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3((unsigned)pairs), dim3(kDecodeThreads), 0,
-                           a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.a_log,
-                           a.state, (T*)a.o, a.H, pairs);
-    else
-        hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3((unsigned)pairs), dim3(kDecodeThreads), 0,
-                           a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.a_log,
-                           a.state, (T*)a.o, a.H, pairs);
+    if (a.gated && a.out_gate) launch_decode_v<T, DK, DV, true, true>(a, pairs);
+    else if (a.gated) launch_decode_v<T, DK, DV, true, false>(a, pairs);
+    else launch_decode_v<T, DK, DV, false, false>(a, pairs);
     return hipGetLastError();
 }
 

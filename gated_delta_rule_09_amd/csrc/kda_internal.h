@@ -19,6 +19,11 @@ struct DecodeArgs {
     hipStream_t stream;
     bool gated = false;
     const float* a_log = nullptr;
+    // With `out_gate` set (gated decode only), `o` receives
+    // y = Sigmoid(out_gate) * norm_weight * o / sqrt(mean(o^2) + eps) instead of o.
+    const void* out_gate = nullptr;
+    const float* norm_weight = nullptr;
+    float eps = 0.f;
 };
 
 struct PrefillArgs {
@@ -33,7 +38,19 @@ struct PrefillArgs {
     const float* a_log = nullptr;
 };
 
+// y = Sigmoid(gate) * weight * o / sqrt(mean(o^2) + eps) over rows of d_v
+// values; weight may be null (ones); y may alias o or gate.
+struct EpilogueArgs {
+    const void* o; const void* gate; const float* weight;
+    int64_t rows; int32_t d_v; float eps;
+    bool bf16;
+    void* y;
+    hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_epilogue(const EpilogueArgs& a);
+int64_t epilogue_max_rows();
 hipError_t launch_prefill(const PrefillArgs& a);
 
 }  // namespace kda

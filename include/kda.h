@@ -61,7 +61,8 @@ typedef enum {
     KDA_ERR_DTYPE = 3,      /* dtype is not one of kda_dtype                     */
     KDA_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned                  */
     KDA_ERR_NO_DEVICE = 5,  /* no HIP device, or the current device is not gfx950 */
-    KDA_ERR_HIP = 6         /* a HIP runtime call failed                          */
+    KDA_ERR_HIP = 6,        /* a HIP runtime call failed                          */
+    KDA_ERR_VALUE = 7       /* a scalar argument is out of range (e.g. eps < 0)   */
 } kda_status;
 
 typedef enum {
@@ -70,7 +71,7 @@ typedef enum {
 } kda_dtype;
 
 /* Version of this interface; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 int kda_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -168,6 +169,64 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
                                  float* state, int32_t N, int32_t H,
                                  int32_t d_k, int32_t d_v, kda_dtype dtype,
                                  void* o, void* stream);
+
+/*
+ * Output epilogue (section 1.3 of the notes, full-rank output gate): the
+ * recurrent output is normalised head-wise with RMSNorm and multiplied by a
+ * sigmoid gate computed from the layer input, before the output projection:
+ *
+ *     y = Sigmoid(gate) * w * o / sqrt(mean(o^2) + eps)
+ *
+ * over the d_v channels of every (token, head) row.  The norm is the one of
+ * the "MoE RMSNorm" page (mean of squares plus eps under the root, a learned
+ * per-channel gain w; the model uses eps = 1e-5), with fp32 arithmetic.  The
+ * gate logits are the output of the projection W_g x (outside this library),
+ * laid out like o.
+ *
+ *   o, gate_logits : [rows, d_v] (rows = T * H; [T, H, d_v] is the same
+ *                    memory), element type given by `dtype`.
+ *   norm_weight    : [d_v] float32 gain shared by the heads, or NULL for 1.
+ *   rows           : >= 0 (0 is a no-op).   d_v: 64 or 128.
+ *   eps            : finite, >= 0, else KDA_ERR_VALUE.  With eps = 0 an
+ *                    all-zero row gives NaN, as the formula does.
+ *   y              : [rows, d_v] output, element type `dtype`.  May alias o or
+ *                    gate_logits exactly (in place); no other overlap.
+ *   stream         : hipStream_t to enqueue on.
+ */
+kda_status kda_output_gate_rmsnorm(const void* o, const void* gate_logits, const float* norm_weight,
+                                   int64_t rows, int32_t d_v, float eps, kda_dtype dtype,
+                                   void* y, void* stream);
+
+/*
+ * The gated prefill followed by the output epilogue: y receives the epilogue
+ * of the prefill's o (o itself is not returned).  Arguments as for
+ * kda_chunk_prefill_gated and kda_output_gate_rmsnorm; out_gate_logits is
+ * [total_T, H, d_v] in `dtype` and must not overlap y.  Two kernels on
+ * `stream`: the prefill writes o into y, the epilogue rewrites y in place, so
+ * no memory beyond the caller's is used.  All arguments are validated before
+ * the first launch.
+ */
+kda_status kda_chunk_prefill_gated_epilogue(const void* q, const void* k, const void* v,
+                                            const void* g_logits, const float* a_log, const float* beta_logits,
+                                            const void* out_gate_logits, const float* norm_weight, float eps,
+                                            const float* init_state, const int32_t* cu_seqlens,
+                                            int32_t N, int64_t total_T, int32_t H,
+                                            int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                            void* y, float* final_state, void* stream);
+
+/*
+ * The gated decode step with the output epilogue fused into the same kernel
+ * (a pair's whole output row lives in one workgroup): y [N, H, d_v] receives
+ * Sigmoid(out_gate) * w * o / sqrt(mean(o^2) + eps) of the step's o; the
+ * state is updated in place as by kda_decode_step_gated.  out_gate_logits is
+ * [N, H, d_v] in `dtype`; norm_weight, eps as for kda_output_gate_rmsnorm.
+ */
+kda_status kda_decode_step_gated_epilogue(const void* q, const void* k, const void* v,
+                                          const void* g_logits, const float* a_log, const float* beta_logits,
+                                          const void* out_gate_logits, const float* norm_weight, float eps,
+                                          float* state, int32_t N, int32_t H,
+                                          int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                          void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -234,3 +234,41 @@ def decode_gated_inputs(N: int, H: int, d: int, dtype: str = "bf16", seed: int =
     ga = _generator(seed * 7 + 101, device)
     a = 2.0 * torch.rand((H,), generator=ga, device=device) - 1.0
     return dict(q=base["q"], k=base["k"], v=base["v"], g_logits=z, a_log=a, beta_logits=b)
+
+
+# ---- inputs of the output epilogue ------------------------------------------
+# Recipe: the output o ~ N(0, 1) per channel times a per-row scale 10^U[-3, 1]
+# (rows from 1e-3, where the mean square is a tenth of epsilon = 1e-5 and the
+# epsilon term dominates, to 10), in the working dtype; gate logits
+# W_g x ~ N(0, 2^2) in the working dtype (Sigmoid spans nearly all of (0, 1));
+# the RMSNorm gain w ~ U[0.5, 1.5], fp32, one per channel.
+
+def epilogue_inputs(shape: Sequence[int], dtype: str = "bf16", seed: int = 0, device="cpu",
+                    slab_rows: int = 1 << 22) -> dict:
+    """o, gate logits [*shape] and gain [shape[-1]] for the output epilogue (recipe above)."""
+    shape = tuple(int(s) for s in shape)
+    d = shape[-1]
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    dt = torch_dtype(dtype)
+    g = _generator(seed * 31 + 977, device)
+    o = torch.empty((rows, d), dtype=dt, device=device)
+    gl = torch.empty((rows, d), dtype=dt, device=device)
+    for r0 in range(0, rows, slab_rows):
+        r1 = min(rows, r0 + slab_rows)
+        scale = 10.0 ** (4.0 * torch.rand((r1 - r0, 1), generator=g, device=device) - 3.0)
+        o[r0:r1] = (torch.randn((r1 - r0, d), generator=g, device=device) * scale).to(dt)
+        gl[r0:r1] = (2.0 * torch.randn((r1 - r0, d), generator=g, device=device)).to(dt)
+    w = 0.5 + torch.rand((d,), generator=g, device=device)
+    return dict(o=o.view(shape), gate=gl.view(shape), weight=w)
+
+
+def out_gate_inputs(shape: Sequence[int], dtype: str = "bf16", seed: int = 0, step: int = 0, device="cpu") -> dict:
+    """Gate logits [*shape] and gain [shape[-1]] for the fused epilogue entry points
+    (laws of the recipe above; the gain depends on ``seed`` only)."""
+    shape = tuple(int(s) for s in shape)
+    dt = torch_dtype(dtype)
+    g = _generator(seed * 31 + 983 + 7919 * step, device)
+    gl = (2.0 * torch.randn(shape, generator=g, device=device)).to(dt)
+    gw = _generator(seed * 31 + 991, device)
+    w = 0.5 + torch.rand((shape[-1],), generator=gw, device=device)
+    return dict(gate=gl, weight=w)

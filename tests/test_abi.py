@@ -32,8 +32,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.kda_abi_version() == 2
-    for s in range(7):
+    assert lib.kda_abi_version() == L.ABI_VERSION == 3
+    for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
 
@@ -106,10 +106,66 @@ def test_gated_decode_rejects_bad_arguments_before_touching_the_device(kw, code)
     assert decode_gated(L.load(), **kw) == code
 
 
+def epilogue(lib, **kw):
+    a = dict(o=P, g=P, w=None, rows=96, dv=128, eps=1e-5, dt=L.KDA_BF16, y=P)
+    a.update(kw)
+    return lib.kda_output_gate_rmsnorm(a["o"], a["g"], a["w"], a["rows"], a["dv"], a["eps"], a["dt"], a["y"], None)
+
+
+def prefill_epi(lib, **kw):
+    a = dict(q=P, k=P, v=P, z=P, A=P, b=P, og=P, w=None, eps=1e-5, init=None, cu=None, N=1, T=64, H=2, dk=64,
+             dv=64, dt=L.KDA_BF16, y=P, fin=P)
+    a.update(kw)
+    return lib.kda_chunk_prefill_gated_epilogue(a["q"], a["k"], a["v"], a["z"], a["A"], a["b"], a["og"], a["w"],
+                                                a["eps"], a["init"], a["cu"], a["N"], a["T"], a["H"], a["dk"],
+                                                a["dv"], a["dt"], a["y"], a["fin"], None)
+
+
+def decode_epi(lib, **kw):
+    a = dict(q=P, k=P, v=P, z=P, A=P, b=P, og=P, w=None, eps=1e-5, S=P, N=4, H=2, dk=64, dv=64, dt=L.KDA_BF16,
+             y=P)
+    a.update(kw)
+    return lib.kda_decode_step_gated_epilogue(a["q"], a["k"], a["v"], a["z"], a["A"], a["b"], a["og"], a["w"],
+                                              a["eps"], a["S"], a["N"], a["H"], a["dk"], a["dv"], a["dt"], a["y"],
+                                              None)
+
+
+NAN, INF = float("nan"), float("inf")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), 3), (dict(dv=96), 2), (dict(rows=-1), 2), (dict(rows=1 << 62), 2), (dict(eps=-1e-5), 7),
+    (dict(eps=NAN), 7), (dict(eps=INF), 7), (dict(o=None), 1), (dict(g=None), 1), (dict(y=None), 1),
+    (dict(o=MIS), 4), (dict(g=MIS), 4), (dict(y=MIS), 4), (dict(w=MIS), 4),
+])
+def test_epilogue_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert epilogue(L.load(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), 3), (dict(dv=96), 2), (dict(N=2), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(eps=-1.0), 7),
+    (dict(og=None), 1), (dict(z=None), 1), (dict(A=None), 1), (dict(og=MIS), 4), (dict(w=MIS), 4),
+    (dict(y=MIS), 4),
+])
+def test_prefill_epilogue_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert prefill_epi(L.load(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=-1), 3), (dict(dk=32), 2), (dict(eps=NAN), 7), (dict(og=None), 1), (dict(A=None), 1),
+    (dict(og=MIS), 4), (dict(w=MIS), 4),
+])
+def test_decode_epilogue_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert decode_epi(L.load(), **kw) == code
+
+
 def test_empty_calls_are_no_ops():
     lib = L.load()
     assert decode(lib, N=0, q=None, S=None) == 0
     assert prefill(lib, T=0, q=None, k=None, v=None, la=None, b=None, o=None, fin=None) == 0
+    assert epilogue(lib, rows=0, o=None, g=None, y=None) == 0
+    assert decode_epi(lib, N=0, q=None, S=None, og=None, y=None) == 0
+    assert prefill_epi(lib, T=0, q=None, k=None, v=None, z=None, b=None, og=None, y=None, fin=None) == 0
 
 
 def _has_gpu():
@@ -126,6 +182,9 @@ def test_valid_call_without_a_device_reports_no_device():
     assert decode(L.load()) == 5
     assert prefill_gated(L.load()) == 5
     assert decode_gated(L.load()) == 5
+    assert epilogue(L.load()) == 5
+    assert prefill_epi(L.load()) == 5
+    assert decode_epi(L.load()) == 5
 
 
 def test_binding_raises_when_library_missing(tmp_path):

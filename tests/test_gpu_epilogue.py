@@ -1,0 +1,222 @@
+"""Parity of the HIP output epilogue (Sigmoid(W_g x) * RMSNorm(o), head-wise;
+"Kimi K3 -- Architecture Notes", section 1.3) with the fp64 oracle (MI355X):
+the standalone kernel, the gated prefill followed by it, and the gated decode
+with it fused."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import oracle
+from gpu_util import TOL, announce, device, host, rel_err
+from gated_delta_rule_09_amd import (RMS_EPS, kda_chunk_prefill_gated, kda_chunk_prefill_gated_epilogue,
+                                     kda_decode_step_gated, kda_decode_step_gated_epilogue, kda_output_gate_rmsnorm)
+
+pytestmark = pytest.mark.gpu
+
+# Element-wise bound of the standalone kernel: its inputs are exact in both
+# dtypes, it computes in fp32 with a handful of operations accurate to about
+# one ulp (~5e-7 relative in all), and rounding to bf16 (8 significant bits,
+# u = 2^-8, to nearest) adds at most u / (1 + u) relative.
+ELEM_TOL = {"f32": 1e-5, "bf16": 2.0 ** -8}
+
+
+def check_elementwise(y, y_ref, dtype, what):
+    y = np.asarray(y, np.float64)
+    err = np.abs(y - y_ref)
+    worst = float((err / np.maximum(np.abs(y_ref), 1e-30)).max())
+    announce(f"  {what}: worst element-wise rel err {worst:.3e} (bound {ELEM_TOL[dtype]:.1e}), "
+             f"norm-wise {rel_err(y, y_ref):.3e}")
+    assert np.isfinite(y).all()
+    assert (err <= ELEM_TOL[dtype] * np.abs(y_ref) + 1e-30).all(), f"{what}: worst {worst}"
+
+
+@pytest.mark.parametrize("rows", [1, 3, 37, 1000, 4096 + 5])
+@pytest.mark.parametrize("d_v", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_epilogue_ragged_rows(rows, d_v, dtype):
+    announce(f"epilogue rows={rows} d_v={d_v} {dtype}")
+    x = ki.epilogue_inputs((rows, d_v), dtype, seed=rows + d_v, device=device())
+    for w in (None, x["weight"]):
+        y = kda_output_gate_rmsnorm(x["o"], x["gate"], w)
+        torch.cuda.synchronize()
+        ref = oracle.kda_output_gate_rmsnorm(host(x["o"]), host(x["gate"]), None if w is None else host(w), RMS_EPS)
+        check_elementwise(host(y), ref, dtype, "no gain" if w is None else "gain")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_epilogue_in_place_and_eps(dtype):
+    announce(f"epilogue in place, eps variants, {dtype}")
+    x = ki.epilogue_inputs((33, 5, 128), dtype, seed=7, device=device())
+    for eps in (0.0, 1e-6, RMS_EPS, 0.5):
+        o = x["o"].clone()
+        y = kda_output_gate_rmsnorm(o, x["gate"], x["weight"], eps=eps, y=o)
+        torch.cuda.synchronize()
+        assert y.data_ptr() == o.data_ptr()
+        ref = oracle.kda_output_gate_rmsnorm(host(x["o"]), host(x["gate"]), host(x["weight"]), eps)
+        check_elementwise(host(y), ref, dtype, f"in place eps={eps}")
+
+
+def test_epilogue_zero_rows_and_extreme_gates():
+    announce("epilogue: all-zero rows, saturated gates")
+    d = 128
+    o = torch.zeros((4, d), dtype=torch.bfloat16, device=device())
+    o[1] = 3.0
+    o[3, ::2] = -1e-20
+    g = torch.zeros((4, d), dtype=torch.bfloat16, device=device())
+    g[:, :32] = 100.0
+    g[:, 32:64] = -100.0
+    y = kda_output_gate_rmsnorm(o, g)
+    torch.cuda.synchronize()
+    ref = oracle.kda_output_gate_rmsnorm(host(o), host(g), None, RMS_EPS)
+    assert (host(y)[0] == 0).all() and (host(y)[2] == 0).all(), "a zero row must stay zero"
+    check_elementwise(host(y), ref, "bf16", "zero rows / saturated gates")
+
+
+def test_epilogue_long_64k_sampled_rows():
+    """The 65,536-token x 96-head bf16 shape in the launch configuration the
+    benchmark times; 8,192 seeded rows are compared (the norm is per row, so
+    a sampled row's oracle value is exact)."""
+    T, H, d = 65536, 96, 128
+    announce(f"epilogue 64K: rows={T * H} d_v={d} bf16")
+    x = ki.epilogue_inputs((T, H, d), "bf16", seed=64, device=device())
+    y = kda_output_gate_rmsnorm(x["o"], x["gate"], x["weight"])
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(np.sort(np.random.default_rng(64).choice(T * H, 8192, replace=False))).to(device())
+    o2, g2, y2 = (t.view(T * H, d)[rows] for t in (x["o"], x["gate"], y))
+    ref = oracle.kda_output_gate_rmsnorm(host(o2), host(g2), host(x["weight"]), RMS_EPS)
+    check_elementwise(host(y2), ref, "bf16", "64K sampled rows")
+    # every row is finite; a zero gain keeps a row's output zero
+    assert bool(torch.isfinite(y).all())
+
+
+def check_through_norm(y, y_ref, o_gpu, o_ref, weight, dtype, what):
+    """y of a fused entry point against the oracle, with the error of the o it
+    normalised carried through the norm.
+
+    o_gpu is the output of the matching unfused entry point on the same
+    inputs, held to the suite's o tolerance here; it only sizes the error
+    budget.  With s(o) = sqrt(mean(o^2) + eps), the map f(o) = o / s(o)
+    satisfies |f(o) - f(o_ref)|_2 <= 2 |o - o_ref|_2 / s(o_ref) for every o
+    (s is 1/sqrt(d)-Lipschitz and |o|_2 <= sqrt(d) s(o)); the gate and the gain
+    scale each channel by at most max|w|, and rounding y to the working dtype
+    adds u |y|.  The o the fused kernel normalises differs from the stored
+    o_gpu by at most the output rounding (u |o_gpu|), so each row must satisfy
+        |y - y_ref|_2 <= (1 + u) 2 max|w| (|o_gpu - o_ref|_2 + u |o_gpu|_2) / s(o_ref)
+                         + (u + 1e-6) |y_ref|_2.
+    A row whose o is small next to the rest is ill-conditioned (the norm
+    magnifies its absolute error by 1 / s), and only such rows get a budget
+    much wider than u."""
+    y = np.asarray(y, np.float64)
+    o_gpu = np.asarray(o_gpu, np.float64)
+    eo = rel_err(o_gpu, o_ref)
+    assert eo <= TOL[dtype], f"{what}: o rel err {eo}"
+    u = ELEM_TOL[dtype]
+    wmax = 1.0 if weight is None else float(np.abs(weight).max())
+    nrm = lambda a: np.sqrt(np.sum(a * a, axis=-1))
+    s_ref = np.sqrt(np.mean(o_ref * o_ref, axis=-1) + RMS_EPS)
+    err = nrm(y - y_ref)
+    bound = ((1 + u) * 2.0 * wmax * (nrm(o_gpu - o_ref) + u * nrm(o_gpu)) / s_ref + (u + 1e-6) * nrm(y_ref))
+    ratio = err / bound
+    i = np.unravel_index(np.argmax(ratio), ratio.shape)
+    announce(f"  {what}: o rel err {eo:.3e}; y norm-wise rel err {rel_err(y, y_ref):.3e}; worst row "
+             f"{tuple(int(j) for j in i)}: |dy| {err[i]:.3e} of budget {bound[i]:.3e} (row rms {s_ref[i]:.3e}, "
+             f"max|o| {np.abs(o_ref).max():.3e}); median |dy|/|y| {np.median(err / nrm(y_ref)):.2e}")
+    assert np.isfinite(y).all()
+    assert (ratio <= 1.0).all(), f"{what}: y beyond the error carried from o"
+
+
+def check_prefill_epilogue(x, og, dtype, heads=None, what=""):
+    announce(f"prefill+epilogue {what}: lengths={x.lengths[:4]}{'...' if len(x.lengths) > 4 else ''} "
+             f"H={x.q.shape[1]} d_k={x.q.shape[2]} d_v={x.v.shape[2]} {dtype}")
+    y, fin = kda_chunk_prefill_gated_epilogue(x.q, x.k, x.v, x.g_logits, x.a_log, x.beta_logits, og["gate"],
+                                              og["weight"], init_state=x.init_state, cu_seqlens=x.cu_seqlens)
+    o_gpu, _ = kda_chunk_prefill_gated(x.q, x.k, x.v, x.g_logits, x.a_log, x.beta_logits, x.init_state,
+                                       x.cu_seqlens, output_final_state=False)
+    torch.cuda.synchronize()
+    hs = slice(None) if heads is None else list(heads)
+    o_ref, f_ref = oracle.kda_prefill_gated(host(x.q), host(x.k), host(x.v), host(x.g_logits), host(x.a_log),
+                                            host(x.beta_logits), host(x.init_state), host(x.cu_seqlens),
+                                            heads=heads)
+    y_ref = oracle.kda_output_gate_rmsnorm(o_ref, host(og["gate"])[:, hs], host(og["weight"]), RMS_EPS)
+    ef = rel_err(host(fin)[:, hs], f_ref)
+    announce(f"  rel err final={ef:.3e} (tol {TOL[dtype]})")
+    check_through_norm(host(y)[:, hs], y_ref, host(o_gpu)[:, hs], o_ref, host(og["weight"]), dtype, "y")
+    assert ef <= TOL[dtype]
+
+
+@pytest.mark.parametrize("lengths", [[1], [65], [128 + 17], [5, 0, 70, 1, 33]])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_epilogue_ragged(lengths, dtype):
+    d = 64 if dtype == "f32" else 128
+    x = ki.gated_inputs(lengths, H=3, d=d, dtype=dtype, seed=sum(lengths) + 40, device=device(),
+                        packed=len(lengths) > 1)
+    og = ki.out_gate_inputs((sum(lengths), 3, d), dtype, seed=sum(lengths) + 40, device=device())
+    check_prefill_epilogue(x, og, dtype, what=f"ragged {lengths}")
+
+
+def test_prefill_epilogue_bf16_4k_sampled_heads():
+    x = ki.gated_inputs([4096], H=96, d=128, dtype="bf16", seed=41, device=device())
+    og = ki.out_gate_inputs((4096, 96, 128), "bf16", seed=41, device=device())
+    check_prefill_epilogue(x, og, "bf16", heads=np.random.default_rng(41).choice(96, 4, replace=False),
+                           what="bf16 4K")
+
+
+def test_prefill_epilogue_long_64k_two_heads():
+    x = ki.gated_inputs([65536], H=96, d=128, dtype="bf16", seed=42, device=device())
+    og = ki.out_gate_inputs((65536, 96, 128), "bf16", seed=42, device=device())
+    check_prefill_epilogue(x, og, "bf16", heads=np.random.default_rng(42).choice(96, 2, replace=False),
+                           what="64K")
+
+
+@pytest.mark.parametrize("dtype,d,d_v", [("bf16", 128, 128), ("f32", 64, 128), ("bf16", 128, 64),
+                                         ("f32", 64, 64)])
+def test_decode_epilogue_steps(dtype, d, d_v):
+    N, H, steps = 6, 3, 10
+    announce(f"decode+epilogue N={N} H={H} d_k={d} d_v={d_v} {dtype}, {steps} steps")
+    state = ki.decode_state(N, H, d, seed=43, device=device(), d_v=d_v)
+    ref = host(state).astype(np.float64)
+    for step in range(steps):
+        x = ki.decode_gated_inputs(N, H, d, dtype=dtype, seed=43, step=step, device=device(), d_v=d_v)
+        og = ki.out_gate_inputs((N, H, d_v), dtype, seed=43, step=step, device=device())
+        w = og["weight"] if step % 2 == 0 else None
+        o_gpu = kda_decode_step_gated(x["q"], x["k"], x["v"], x["g_logits"], x["a_log"], x["beta_logits"],
+                                      state.clone())
+        y = kda_decode_step_gated_epilogue(x["q"], x["k"], x["v"], x["g_logits"], x["a_log"], x["beta_logits"],
+                                           og["gate"], state, norm_weight=w)
+        torch.cuda.synchronize()
+        o_ref, ref = oracle.kda_decode_step_gated(host(x["q"]), host(x["k"]), host(x["v"]), host(x["g_logits"]),
+                                                  host(x["a_log"]), host(x["beta_logits"]), ref)
+        y_ref = oracle.kda_output_gate_rmsnorm(o_ref, host(og["gate"]), None if w is None else host(w), RMS_EPS)
+        check_through_norm(host(y), y_ref, host(o_gpu), o_ref, None if w is None else host(w), dtype,
+                           f"step {step}")
+    es = rel_err(host(state), ref)
+    announce(f"  rel err state={es:.3e}")
+    assert es <= TOL[dtype]
+
+
+def test_decode_epilogue_full_shape_sampled_pairs():
+    """512 sequences x 96 heads (the decode benchmark's shape), 3 steps, 64 seeded pairs."""
+    N, H, d = 512, 96, 128
+    announce(f"decode+epilogue full shape N={N} H={H}")
+    state = ki.decode_state(N, H, d, seed=44, device=device())
+    flat = np.random.default_rng(44).choice(N * H, 64, replace=False)
+    ns, hs = torch.tensor(flat // H, device=device()), torch.tensor(flat % H, device=device())
+    ref = host(state[ns, hs]).astype(np.float64)[None]
+    for step in range(3):
+        x = ki.decode_gated_inputs(N, H, d, "bf16", seed=44, step=step, device=device())
+        og = ki.out_gate_inputs((N, H, d), "bf16", seed=44, step=step, device=device())
+        o_gpu = kda_decode_step_gated(x["q"], x["k"], x["v"], x["g_logits"], x["a_log"], x["beta_logits"],
+                                      state.clone())
+        y = kda_decode_step_gated_epilogue(x["q"], x["k"], x["v"], x["g_logits"], x["a_log"], x["beta_logits"],
+                                           og["gate"], state, norm_weight=og["weight"])
+        sel = {kk: host(vv[ns, hs])[None] for kk, vv in x.items() if kk != "a_log"}
+        o_ref, ref = oracle.kda_decode_step_gated(sel["q"], sel["k"], sel["v"], sel["g_logits"],
+                                                  host(x["a_log"])[flat % H], sel["beta_logits"], ref)
+        y_ref = oracle.kda_output_gate_rmsnorm(o_ref, host(og["gate"][ns, hs])[None], host(og["weight"]), RMS_EPS)
+        check_through_norm(host(y[ns, hs])[None], y_ref, host(o_gpu[ns, hs])[None], o_ref, host(og["weight"]),
+                           "bf16", f"step {step}")
+    torch.cuda.synchronize()
+    es = rel_err(host(state[ns, hs])[None], ref)
+    announce(f"  state rel err {es:.3e}")
+    assert es <= TOL["bf16"]
