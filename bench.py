@@ -10,9 +10,11 @@ Inputs are synthetic, seeded, and resident in device memory before timing.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Prints one JSON line.  `value` is prefill tokens/s; decode state-update
-bandwidth is reported under "decode"; the gated entry points and the output
+bandwidth is reported under "decode"; the gated entry points, the output
 epilogue (standalone, after the gated prefill, fused into the gated decode)
-are timed after the headline step under "gated" and "epilogue".  Kernel durations come from HIP events
+and the input prologue (standalone, the whole prefill layer core, the
+one-kernel decode step) are timed after the headline step under "gated",
+"epilogue" and "prologue".  Kernel durations come from HIP events
 recorded on the stream the kernels are launched on.
 """
 
@@ -43,6 +45,12 @@ GATED_DECODE_BYTES_PER_PAIR = 2 * STATE_BYTES + 3 * D * 2 + D * 2 + 4 + D * 2
 EPILOGUE_BYTES_PER_TOKEN_HEAD = 3 * D * 2                                # 768
 # Gated decode with the epilogue fused: the gate logits are read, y replaces o.
 EPILOGUE_DECODE_BYTES_PER_PAIR = GATED_DECODE_BYTES_PER_PAIR + D * 2
+# Input prologue: read x_q, x_k, x_v and write q, k, v (bf16).
+PROLOGUE_BYTES_PER_TOKEN_HEAD = 2 * 3 * D * 2                            # 1536
+CONV_C = 3 * D                                                           # packed channels per head
+# Whole fused decode step: the gated decode with the epilogue, plus the convolution state
+# (3 entries per channel read, 3 written).
+FUSED_DECODE_BYTES_PER_PAIR = EPILOGUE_DECODE_BYTES_PER_PAIR + 2 * 3 * CONV_C * 2
 # Algorithmic flops per token-head, chunk 64, causal triangles only.
 PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 2 * 64 * (D + D)              # 131,072
 
@@ -88,6 +96,8 @@ KERNEL_SOURCES = {
     "decode": ["gated_delta_rule_09_amd/csrc/kda_decode.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
                "gated_delta_rule_09_amd/csrc/kda_internal.h"],
     "epilogue": ["gated_delta_rule_09_amd/csrc/kda_epilogue.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
+                 "gated_delta_rule_09_amd/csrc/kda_internal.h"],
+    "prologue": ["gated_delta_rule_09_amd/csrc/kda_prologue.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
                  "gated_delta_rule_09_amd/csrc/kda_internal.h"],
 }
 
@@ -193,6 +203,56 @@ def time_epilogue(args, dev, stream, ki, lib):
                       "512 x 96 gated decode"}
 
 
+def time_prologue(args, dev, stream, ki, lib):
+    """The input prologue (ShortConv(4), Swish, L2 norm of q and k): the standalone
+    kernel on the 64K x 96-head inputs, the whole prefill layer core (prologue,
+    gated prefill, epilogue) and the one-kernel fused decode step."""
+    import torch
+    reps = max(1, args.steps)
+    x = ki.prologue_inputs([T_PREFILL], H=H, d=D, dtype="bf16", seed=3, device=dev)
+    q, k, v = torch.empty_like(x["x_q"]), torch.empty_like(x["x_k"]), torch.empty_like(x["x_v"])
+    cso = torch.empty_like(x["conv_state"])
+    pro_ms = _timed(args, stream, lambda: lib.kda_short_conv_prologue(
+        x["x_q"], x["x_k"], x["x_v"], x["conv_w"], x["conv_state"], q=q, k=k, v=v, conv_state_out=cso), reps)
+    pro_bytes = T_PREFILL * H * PROLOGUE_BYTES_PER_TOKEN_HEAD + 2 * H * 3 * CONV_C * 2 + H * CONV_C * 16
+    xg = ki.gated_inputs([T_PREFILL], H=H, d=D, dtype="bf16", seed=3, device=dev)
+    og = ki.out_gate_inputs((T_PREFILL, H, D), "bf16", seed=3, device=dev)
+    y = torch.empty_like(xg.v)
+    fin = torch.empty_like(xg.init_state)
+
+    def layer():
+        lib.kda_short_conv_prologue(x["x_q"], x["x_k"], x["x_v"], x["conv_w"], x["conv_state"], q=q, k=k, v=v,
+                                    conv_state_out=cso)
+        lib.kda_chunk_prefill_gated_epilogue(q, k, v, xg.g_logits, xg.a_log, xg.beta_logits, og["gate"],
+                                             og["weight"], init_state=xg.init_state, y=y, final_state=fin)
+
+    layer_ms = _timed(args, stream, layer, reps)
+    del x, q, k, v, cso, xg, og, y, fin
+    w = ki.DECODE_WORKLOAD
+    sg = ki.decode_state(w["N"], w["H"], w["d"], seed=w["seed"], device=dev)
+    dp = ki.decode_prologue_inputs(w["N"], w["H"], w["d"], "bf16", seed=w["seed"], device=dev)
+    dg = ki.decode_gated_inputs(w["N"], w["H"], w["d"], dtype=w["dtype"], seed=w["seed"], step=0, device=dev)
+    dog = ki.out_gate_inputs((w["N"], w["H"], w["d"]), "bf16", seed=w["seed"], device=dev)
+    yd = torch.empty_like(dp["x_v"])
+    dec_ms = _timed(args, stream, lambda: lib.kda_decode_step_fused(
+        dp["x_q"], dp["x_k"], dp["x_v"], dp["conv_w"], dp["conv_state"], dg["g_logits"], dg["a_log"],
+        dg["beta_logits"], dog["gate"], sg, norm_weight=dog["weight"], y=yd), reps)
+    dec_bytes = N_DECODE * H * FUSED_DECODE_BYTES_PER_PAIR + H * CONV_C * 16
+    pro_gbps = pro_bytes / (pro_ms * 1e-3) / 1e9
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    return {"standalone": {"ms": round(pro_ms, 4), "gbps": round(pro_gbps, 1),
+                           "frac": round(pro_gbps / HBM_PEAK_GBPS, 4),
+                           "traffic": measured_traffic("prologue", pro_ms),
+                           "bytes_per_token_head": PROLOGUE_BYTES_PER_TOKEN_HEAD, "kernel": "prologue_kernel"},
+            "prefill_layer": {"ms": round(layer_ms, 4), "tokens_per_s": round(T_PREFILL / (layer_ms * 1e-3), 1),
+                              "kernels": "prologue, gated prefill, epilogue"},
+            "decode_fused": {"ms": round(dec_ms, 4), "gbps": round(dec_gbps, 1),
+                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                             "bytes_per_pair": FUSED_DECODE_BYTES_PER_PAIR},
+            "config": "x_q, x_k, x_v ~ N(0, 1) bf16, taps ~ U[-1/2, 1/2], conv state ~ N(0, 1); 64K x 96 x 128 "
+                      "prefill and the 512 x 96 decode"}
+
+
 def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
     """The gated entry points (decay / write-strength logits mapped in-kernel) on the
     same 64K prefill and 512 x 96 decode shapes, timed outside the headline step."""
@@ -232,7 +292,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gated", action="store_true", help="skip the timing of the gated entry points")
-    ap.add_argument("--no-epilogue", action="store_true", help="skip the timing of the output epilogue")
+    ap.add_argument("--no-epilogue", action="store_true",
+                    help="skip the timing of the output epilogue and the input prologue")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -340,6 +401,8 @@ def main():
         torch.cuda.empty_cache()
         import gated_delta_rule_09_amd as lib
         res["epilogue"] = time_epilogue(args, dev, stream, ki, lib)
+        torch.cuda.empty_cache()
+        res["prologue"] = time_prologue(args, dev, stream, ki, lib)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)

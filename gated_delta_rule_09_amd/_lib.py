@@ -49,6 +49,10 @@ SIGNATURES = {
                                                          _VP, _VP, _VP]),
     "kda_decode_step_gated_epilogue": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP,
                                                        _I32, _I32, _I32, _I32, ctypes.c_int, _VP, _VP]),
+    "kda_short_conv_prologue": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
+                                                ctypes.c_int, _VP, _VP, _VP, _VP, _VP]),
+    "kda_decode_step_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP,
+                                              _I32, _I32, _I32, _I32, ctypes.c_int, _VP, _VP]),
 }
 
 _lib = None
@@ -353,4 +357,78 @@ def kda_decode_step_gated_epilogue(q: torch.Tensor, k: torch.Tensor, v: torch.Te
                                             _stream_handle(dev))
     if st != KDA_OK:
         raise KDAError("kda_decode_step_gated_epilogue", st)
+    return y
+
+
+def kda_short_conv_prologue(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor, conv_w: torch.Tensor,
+                            conv_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                            q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
+                            v: Optional[torch.Tensor] = None, conv_state_out: Optional[torch.Tensor] = None,
+                            output_conv_state: bool = True):
+    """Short convolution, Swish and the L2 norm of q and k (see include/kda.h,
+    kda_short_conv_prologue).  Returns (q, k, v, conv_state_out)."""
+    lib = load()
+    T, H, d_k = x_q.shape
+    d_v = x_v.shape[2]
+    dev, dt = x_q.device, x_q.dtype
+    code = _dtype_code(dt)
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    C = 2 * d_k + d_v
+    _check(x_q, "x_q", (T, H, d_k), dt, dev)
+    _check(x_k, "x_k", (T, H, d_k), dt, dev)
+    _check(x_v, "x_v", (T, H, d_v), dt, dev)
+    _check(conv_w, "conv_w", (H, C, 4), torch.float32, dev)
+    if conv_state is not None:
+        _check(conv_state, "conv_state", (N, 3, H, C), dt, dev)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    q = torch.empty_like(x_q) if q is None else q
+    k = torch.empty_like(x_k) if k is None else k
+    v = torch.empty_like(x_v) if v is None else v
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(k, "k", (T, H, d_k), dt, dev)
+    _check(v, "v", (T, H, d_v), dt, dev)
+    if output_conv_state and conv_state_out is None:
+        conv_state_out = torch.empty((N, 3, H, C), dtype=dt, device=dev)
+    if conv_state_out is not None:
+        _check(conv_state_out, "conv_state_out", (N, 3, H, C), dt, dev)
+    st = lib.kda_short_conv_prologue(_ptr(x_q), _ptr(x_k), _ptr(x_v), _ptr(conv_w), _ptr(conv_state),
+                                     _ptr(cu_seqlens), N, T, H, d_k, d_v, code, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(conv_state_out), _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_short_conv_prologue", st)
+    return q, k, v, conv_state_out
+
+
+def kda_decode_step_fused(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor, conv_w: torch.Tensor,
+                          conv_state: torch.Tensor, g_logits: torch.Tensor, a_log: torch.Tensor,
+                          beta_logits: torch.Tensor, out_gate_logits: torch.Tensor, state: torch.Tensor,
+                          norm_weight: Optional[torch.Tensor] = None, eps: float = RMS_EPS,
+                          y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One whole decode step (prologue, gate maps, recurrence, epilogue) in one
+    kernel; ``conv_state`` and ``state`` are updated in place.  Returns y [N, H, d_v]."""
+    lib = load()
+    N, H, d_k = x_q.shape
+    d_v = x_v.shape[2]
+    dev, dt = x_q.device, x_q.dtype
+    code = _dtype_code(dt)
+    C = 2 * d_k + d_v
+    _check(x_q, "x_q", (N, H, d_k), dt, dev)
+    _check(x_k, "x_k", (N, H, d_k), dt, dev)
+    _check(x_v, "x_v", (N, H, d_v), dt, dev)
+    _check(conv_w, "conv_w", (H, C, 4), torch.float32, dev)
+    _check(conv_state, "conv_state", (N, 3, H, C), dt, dev)
+    _check(g_logits, "g_logits", (N, H, d_k), dt, dev)
+    _check(a_log, "a_log", (H,), torch.float32, dev)
+    _check(beta_logits, "beta_logits", (N, H), torch.float32, dev)
+    _check_epilogue_args(out_gate_logits, norm_weight, (N, H, d_v), dt, dev)
+    _check(state, "state", (N, H, d_k, d_v), torch.float32, dev)
+    if y is None:
+        y = torch.empty((N, H, d_v), dtype=dt, device=dev)
+    _check(y, "y", (N, H, d_v), dt, dev)
+    st = lib.kda_decode_step_fused(_ptr(x_q), _ptr(x_k), _ptr(x_v), _ptr(conv_w), _ptr(conv_state), _ptr(g_logits),
+                                   _ptr(a_log), _ptr(beta_logits), _ptr(out_gate_logits), _ptr(norm_weight),
+                                   float(eps), _ptr(state), N, H, d_k, d_v, code, _ptr(y), _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_decode_step_fused", st)
     return y

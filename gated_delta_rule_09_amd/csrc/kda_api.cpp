@@ -85,23 +85,27 @@ kda_status decode_impl(const char* name, const void* q, const void* k, const voi
                        const float* beta, const float* a_log, bool gated, float* state, int32_t N, int32_t H,
                        int32_t d_k, int32_t d_v, kda_dtype dtype, void* o, void* stream,
                        bool epilogue = false, const void* out_gate = nullptr, const float* norm_weight = nullptr,
-                       float eps = 0.f) {
+                       float eps = 0.f, bool prologue = false, const float* conv_w = nullptr,
+                       void* conv_state = nullptr) {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (N < 0 || H < 1 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
     if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
     if (epilogue && !valid_eps(eps)) return KDA_ERR_VALUE;
     if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !decay || !beta || !state || !o || (gated && !a_log) || (epilogue && !out_gate))
+    if (!q || !k || !v || !decay || !beta || !state || !o || (gated && !a_log) || (epilogue && !out_gate) ||
+        (prologue && (!conv_w || !conv_state)))
         return KDA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(decay) ||
         !aligned16(beta) || !aligned16(state) || !aligned16(o) || (gated && !aligned16(a_log)) ||
-        (epilogue && !aligned16(out_gate)) || (norm_weight && !aligned16(norm_weight)))
+        (epilogue && !aligned16(out_gate)) || (norm_weight && !aligned16(norm_weight)) ||
+        (prologue && (!aligned16(conv_w) || !aligned16(conv_state))))
         return KDA_ERR_ALIGN;
     kda_status st = check_device();
     if (st != KDA_OK) return st;
     kda::DecodeArgs a{q, k, v, decay, beta, state, o, N, H, d_k, d_v,
                       dtype == KDA_BF16, reinterpret_cast<hipStream_t>(stream), gated, a_log,
-                      epilogue ? out_gate : nullptr, norm_weight, eps};
+                      epilogue ? out_gate : nullptr, norm_weight, eps,
+                      prologue ? conv_w : nullptr, prologue ? conv_state : nullptr};
     hipError_t e = kda::launch_decode(a);
     if (e != hipSuccess) {
         set_error(name, e);
@@ -241,6 +245,49 @@ kda_status kda_decode_step_gated_epilogue(const void* q, const void* k, const vo
                                           void* y, void* stream) {
     return decode_impl("kda_decode_step_gated_epilogue launch", q, k, v, g_logits, beta_logits, a_log, true, state,
                        N, H, d_k, d_v, dtype, y, stream, true, out_gate_logits, norm_weight, eps);
+}
+
+kda_status kda_decode_step_fused(const void* x_q, const void* x_k, const void* x_v,
+                                 const float* conv_w, void* conv_state,
+                                 const void* g_logits, const float* a_log, const float* beta_logits,
+                                 const void* out_gate_logits, const float* norm_weight, float eps,
+                                 float* state, int32_t N, int32_t H,
+                                 int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                 void* y, void* stream) {
+    return decode_impl("kda_decode_step_fused launch", x_q, x_k, x_v, g_logits, beta_logits, a_log, true, state,
+                       N, H, d_k, d_v, dtype, y, stream, true, out_gate_logits, norm_weight, eps, true, conv_w,
+                       conv_state);
+}
+
+kda_status kda_short_conv_prologue(const void* x_q, const void* x_k, const void* x_v, const float* conv_w,
+                                   const void* conv_state_in, const int32_t* cu_seqlens,
+                                   int32_t N, int64_t total_T, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype dtype, void* q, void* k, void* v, void* conv_state_out,
+                                   void* stream) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (N < 1 || H < 1 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
+    if (cu_seqlens == nullptr && N != 1) return KDA_ERR_SHAPE;
+    if (H > 65535 || !kda::prologue_grid_fits(total_T, H)) return KDA_ERR_SHAPE;
+    if (total_T > 0 && (!x_q || !x_k || !x_v || !conv_w || !q || !k || !v)) return KDA_ERR_NULL;
+    const void* ptrs[] = {x_q, x_k, x_v, conv_w, conv_state_in, cu_seqlens, q, k, v, conv_state_out};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    if (conv_state_in && conv_state_out) {
+        const uintptr_t bytes = (uintptr_t)N * 3 * H * (2 * d_k + d_v) * (dtype == KDA_BF16 ? 2 : 4);
+        const uintptr_t a = reinterpret_cast<uintptr_t>(conv_state_in), b = reinterpret_cast<uintptr_t>(conv_state_out);
+        if (a < b + bytes && b < a + bytes) return KDA_ERR_VALUE;     // the two states overlap
+    }
+    if (total_T == 0 && conv_state_out == nullptr) return KDA_OK;
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    kda::PrologueArgs a{x_q, x_k, x_v, conv_w, conv_state_in, conv_state_out, cu_seqlens, N, total_T, H, d_k, d_v,
+                        dtype == KDA_BF16, q, k, v, reinterpret_cast<hipStream_t>(stream)};
+    hipError_t e = kda::launch_prologue(a);
+    if (e != hipSuccess) {
+        set_error("kda_short_conv_prologue launch", e);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
 }
 
 }  // extern "C"

@@ -24,6 +24,12 @@ struct DecodeArgs {
     const void* out_gate = nullptr;
     const float* norm_weight = nullptr;
     float eps = 0.f;
+    // With `conv_w` set as well (gated decode with the epilogue only), q, k, v
+    // are projection outputs and the input prologue runs first: width-4
+    // convolution (taps [H, 2 d_k + d_v, 4] fp32, state [N, 3, H, 2 d_k + d_v]
+    // in the element type, updated in place), Swish, L2 norm of q and k.
+    const float* conv_w = nullptr;
+    void* conv_state = nullptr;
 };
 
 struct PrefillArgs {
@@ -48,7 +54,24 @@ struct EpilogueArgs {
     hipStream_t stream;
 };
 
+// Input prologue: q = l2(swish(conv x_q)), k = l2(swish(conv x_k)),
+// v = swish(conv x_v), width-4 depthwise causal convolution per head; weights
+// [H, 2 d_k + d_v, 4] fp32, states [N, 3, H, 2 d_k + d_v] in the element type.
+struct PrologueArgs {
+    const void* x_q; const void* x_k; const void* x_v;
+    const float* conv_w;
+    const void* state_in;     // null: zeros
+    void* state_out;          // null: not stored; must not overlap state_in
+    const int32_t* cu_seqlens;
+    int32_t N; int64_t total_T; int32_t H, d_k, d_v;
+    bool bf16;
+    void* q; void* k; void* v;
+    hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prologue(const PrologueArgs& p);
+bool prologue_grid_fits(int64_t total_T, int32_t H);
 hipError_t launch_epilogue(const EpilogueArgs& a);
 int64_t epilogue_max_rows();
 hipError_t launch_prefill(const PrefillArgs& a);

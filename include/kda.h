@@ -228,6 +228,66 @@ kda_status kda_decode_step_gated_epilogue(const void* q, const void* k, const vo
                                           int32_t d_k, int32_t d_v, kda_dtype dtype,
                                           void* y, void* stream);
 
+/*
+ * Input prologue (section 1.1 of the notes; the width comes from the atlas's
+ * KDA page): each of the q, k, v projection outputs passes a depthwise causal
+ * convolution of width 4 and Swish, and q and k are then L2-normalised:
+ *
+ *     conv(x)_t = sum_{j=0..3} w[c, j] x_{t-3+j}[c]   (per head and channel c)
+ *     q = l2(swish(conv x_q)),  k = l2(swish(conv x_k)),  v = swish(conv x_v),
+ *     swish(u) = u Sigmoid(u),  l2(u) = u / sqrt(sum u^2 + 1e-6).
+ *
+ * Inputs before a sequence's first token come from its convolution state:
+ * the last 3 inputs of the previous segment, oldest first (zeros if NULL).
+ * Per head the packed channel order of weights and states is q (d_k
+ * channels), then k (d_k), then v (d_v); C = 2 d_k + d_v.  fp32 arithmetic.
+ *
+ *   x_q, x_k       : [total_T, H, d_k] projection outputs, element type `dtype`.
+ *   x_v            : [total_T, H, d_v].
+ *   conv_w         : [H, C, 4] float32 taps (tap 3 meets the current input).
+ *   conv_state_in  : [N, 3, H, C] in `dtype`, or NULL for zeros.
+ *   cu_seqlens, N, total_T, H, d_k, d_v, dtype : as for kda_chunk_prefill.
+ *   q, k, v        : outputs, shaped like x_q, x_k, x_v (the inputs of
+ *                    kda_chunk_prefill_gated).
+ *   conv_state_out : [N, 3, H, C] final state per sequence (the last 3 inputs,
+ *                    filled from the initial state for sequences shorter than
+ *                    3), or NULL.  It must not overlap conv_state_in
+ *                    (KDA_ERR_VALUE); to continue in place, alternate two
+ *                    buffers.
+ *   stream         : hipStream_t to enqueue on.
+ */
+kda_status kda_short_conv_prologue(const void* x_q, const void* x_k, const void* x_v, const float* conv_w,
+                                   const void* conv_state_in, const int32_t* cu_seqlens,
+                                   int32_t N, int64_t total_T, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype dtype, void* q, void* k, void* v, void* conv_state_out,
+                                   void* stream);
+
+/*
+ * One whole decode step of a KDA layer between its projections: the input
+ * prologue (as kda_short_conv_prologue, one token per sequence, the
+ * convolution state updated in place), the gate maps and the recurrence (as
+ * kda_decode_step_gated) and the output epilogue (as kda_output_gate_rmsnorm),
+ * in one kernel launch; every step of a pair runs in one workgroup.
+ *
+ *   x_q, x_k    : [N, H, d_k] projection outputs, element type `dtype`.
+ *   x_v         : [N, H, d_v].
+ *   conv_w      : [H, 2 d_k + d_v, 4] float32 convolution taps.
+ *   conv_state  : [N, 3, H, 2 d_k + d_v] in `dtype`, read and overwritten in
+ *                 place (the oldest input dropped, this token's appended).
+ *   g_logits, a_log, beta_logits : as for kda_decode_step_gated.
+ *   out_gate_logits, norm_weight, eps : as for kda_decode_step_gated_epilogue.
+ *   state       : [N, H, d_k, d_v] fp32, updated in place.
+ *   y           : [N, H, d_v] output in `dtype`.
+ * No two of x_q, x_k, x_v, conv_state, y may overlap.
+ */
+kda_status kda_decode_step_fused(const void* x_q, const void* x_k, const void* x_v,
+                                 const float* conv_w, void* conv_state,
+                                 const void* g_logits, const float* a_log, const float* beta_logits,
+                                 const void* out_gate_logits, const float* norm_weight, float eps,
+                                 float* state, int32_t N, int32_t H,
+                                 int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                 void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -272,3 +272,52 @@ def out_gate_inputs(shape: Sequence[int], dtype: str = "bf16", seed: int = 0, st
     gw = _generator(seed * 31 + 991, device)
     w = 0.5 + torch.rand((shape[-1],), generator=gw, device=device)
     return dict(gate=gl, weight=w)
+
+
+# ---- inputs of the input prologue -------------------------------------------
+# Recipe: projection outputs x_q, x_k, x_v ~ N(0, 1) in the working dtype;
+# convolution taps ~ U[-1/2, 1/2] fp32 (the default bound 1/sqrt(fan-in) of a
+# width-4 depthwise convolution); initial convolution state ~ N(0, 1) in the
+# working dtype (earlier projection outputs), or none.
+
+def prologue_inputs(lengths: Sequence[int], H: int, d: int, dtype: str = "bf16", seed: int = 0, device="cpu",
+                    d_v: Optional[int] = None, state: bool = True, packed: Optional[bool] = None,
+                    slab: int = 65536) -> dict:
+    """x_q, x_k, x_v, conv_w, conv_state, cu_seqlens for the prologue (recipe above)."""
+    d_v = d if d_v is None else d_v
+    lengths = [int(x) for x in lengths]
+    T, N = sum(lengths), len(lengths)
+    dt = torch_dtype(dtype)
+    g = _generator(seed * 53 + 1201, device)
+    xs = []
+    for dd in (d, d, d_v):
+        x = torch.empty((T, H, dd), dtype=dt, device=device)
+        for t0 in range(0, T, slab):
+            t1 = min(T, t0 + slab)
+            x[t0:t1] = torch.randn((t1 - t0, H, dd), generator=g, device=device).to(dt)
+        xs.append(x)
+    C = 2 * d + d_v
+    w = torch.rand((H, C, 4), generator=g, device=device) - 0.5
+    st = torch.randn((N, 3, H, C), generator=g, device=device).to(dt) if state else None
+    if packed is None:
+        packed = N > 1
+    cu = None
+    if packed:
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device=device)
+    return dict(x_q=xs[0], x_k=xs[1], x_v=xs[2], conv_w=w, conv_state=st, cu_seqlens=cu, lengths=lengths)
+
+
+def decode_prologue_inputs(N: int, H: int, d: int, dtype: str = "bf16", seed: int = 0, step: int = 0, device="cpu",
+                           d_v: Optional[int] = None) -> dict:
+    """Per-step projection outputs x_q, x_k, x_v [N, H, .] (laws of the prologue
+    recipe), and, from ``seed`` alone, the taps [H, C, 4] and the initial
+    convolution state [N, 3, H, C]."""
+    d_v = d if d_v is None else d_v
+    dt = torch_dtype(dtype)
+    g = _generator(seed * 53 + 1301 + 7717 * (step + 1), device)
+    xs = [torch.randn((N, H, dd), generator=g, device=device).to(dt) for dd in (d, d, d_v)]
+    C = 2 * d + d_v
+    gp = _generator(seed * 53 + 1303, device)
+    w = torch.rand((H, C, 4), generator=gp, device=device) - 0.5
+    st = torch.randn((N, 3, H, C), generator=gp, device=device).to(dt)
+    return dict(x_q=xs[0], x_k=xs[1], x_v=xs[2], conv_w=w, conv_state=st)

@@ -159,6 +159,47 @@ def test_decode_epilogue_rejects_bad_arguments_before_touching_the_device(kw, co
     assert decode_epi(L.load(), **kw) == code
 
 
+def prologue(lib, **kw):
+    a = dict(xq=P, xk=P, xv=P, w=P, si=None, cu=None, N=1, T=64, H=2, dk=64, dv=64, dt=L.KDA_BF16, q=P, k=P, v=P,
+             so=None)
+    a.update(kw)
+    return lib.kda_short_conv_prologue(a["xq"], a["xk"], a["xv"], a["w"], a["si"], a["cu"], a["N"], a["T"], a["H"],
+                                       a["dk"], a["dv"], a["dt"], a["q"], a["k"], a["v"], a["so"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), 3), (dict(dk=32), 2), (dict(dv=256), 2), (dict(N=0), 2), (dict(N=2), 2), (dict(H=0), 2),
+    (dict(T=-5), 2), (dict(H=70000), 2), (dict(T=1 << 40, H=4096), 2), (dict(xq=None), 1), (dict(w=None), 1),
+    (dict(v=None), 1), (dict(xv=MIS), 4), (dict(w=MIS), 4), (dict(si=MIS), 4), (dict(so=MIS), 4),
+    (dict(si=P, so=P), 7), (dict(si=ctypes.c_void_p(0x10000), so=ctypes.c_void_p(0x10000 + 16)), 7),
+])
+def test_prologue_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert prologue(L.load(), **kw) == code
+
+
+def test_prologue_accepts_adjacent_states():
+    # [N, 3, H, C] bf16 with N=1, H=2, C=192: 2304 bytes; a state right after the other is fine
+    lib = L.load()
+    st = prologue(lib, si=ctypes.c_void_p(0x10000), so=ctypes.c_void_p(0x10000 + 2304))
+    assert st in (0, 5)     # no overlap: validation passes (5 = no device here)
+
+
+def decode_fused(lib, **kw):
+    a = dict(xq=P, xk=P, xv=P, w=P, cs=P, z=P, A=P, b=P, og=P, g=None, eps=1e-5, S=P, N=4, H=2, dk=64, dv=64,
+             dt=L.KDA_BF16, y=P)
+    a.update(kw)
+    return lib.kda_decode_step_fused(a["xq"], a["xk"], a["xv"], a["w"], a["cs"], a["z"], a["A"], a["b"], a["og"],
+                                     a["g"], a["eps"], a["S"], a["N"], a["H"], a["dk"], a["dv"], a["dt"], a["y"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), 3), (dict(dv=48), 2), (dict(H=0), 2), (dict(eps=-0.5), 7), (dict(w=None), 1), (dict(cs=None), 1),
+    (dict(og=None), 1), (dict(A=None), 1), (dict(w=MIS), 4), (dict(cs=MIS), 4), (dict(g=MIS), 4),
+])
+def test_fused_decode_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert decode_fused(L.load(), **kw) == code
+
+
 def test_empty_calls_are_no_ops():
     lib = L.load()
     assert decode(lib, N=0, q=None, S=None) == 0
@@ -166,6 +207,8 @@ def test_empty_calls_are_no_ops():
     assert epilogue(lib, rows=0, o=None, g=None, y=None) == 0
     assert decode_epi(lib, N=0, q=None, S=None, og=None, y=None) == 0
     assert prefill_epi(lib, T=0, q=None, k=None, v=None, z=None, b=None, og=None, y=None, fin=None) == 0
+    assert prologue(lib, T=0, xq=None, xk=None, xv=None, w=None, q=None, k=None, v=None) == 0
+    assert decode_fused(lib, N=0, xq=None, w=None, cs=None, S=None, y=None) == 0
 
 
 def _has_gpu():
@@ -185,6 +228,8 @@ def test_valid_call_without_a_device_reports_no_device():
     assert epilogue(L.load()) == 5
     assert prefill_epi(L.load()) == 5
     assert decode_epi(L.load()) == 5
+    assert prologue(L.load()) == 5
+    assert decode_fused(L.load()) == 5
 
 
 def test_binding_raises_when_library_missing(tmp_path):
