@@ -33,14 +33,16 @@
 // The waves take one of two roles, and in every chunk iteration both run at
 // once on different chunks:
 //   SI  (state-independent, waves 0-3, chunk c+1): wave i owns tile i.  A lane
-//       owns d_k/32 key channels of 8 of the tile's positions (lanes 0-31 the
-//       first 8, lanes 32-63 the last 8); the running products are formed in
-//       registers and joined across the two halves with one lane exchange.
-//       The wave writes the tile's scaled operands, its P and M (MFMA) and the
-//       16x16 inverse (fp32 substitution on 16 lanes) to one of two LDS
-//       buffers, selected by chunk parity.
+//       owns 8 consecutive key channels (one 16-byte bf16 load) of RP
+//       consecutive positions (d_k = 128: 16 lanes per token row, 4 position
+//       groups of 4 positions); the running products are formed in registers
+//       and joined across the position groups with a butterfly of row swaps.
+//       The wave writes the tile's scaled operands, its P and M (MFMA) and beta
+//       to one of two LDS buffers, selected by chunk parity.
 //   SD  (state-dependent, waves 4-7, chunk c): wave w owns 16 value columns and
-//       walks the chunk's four tiles.  Its slab of S, and U and W, live in MFMA
+//       walks the chunk's four tiles.  Wave 4 + i first forms the 16x16 inverse
+//       of tile i (fp32 substitution on all 64 lanes) and publishes it through
+//       an LDS flag, so the four inverses of a chunk are built in parallel.  Its slab of S, and U and W, live in MFMA
 //       accumulators and are fed back as MFMA operands directly (an accumulator
 //       tile holds 4 consecutive rows per lane, the K-layout of an operand);
 //       the LDS operands are read with the matching row permutation.
