@@ -130,7 +130,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(
 
     float* S = state + pair * (int64_t)(DK * DV);
 
-    // Issue the state loads first: they are the bulk of the traffic.
     // The few per-channel loads go first: the vector memory counter retires
     // loads in order, so their consumers then wait only for them while the
     // state loads, the bulk of the traffic, are still in flight.
