@@ -7,7 +7,7 @@ and beta, fp32 state) followed by one decode step of the batched-decode
 workload (512 sequences x 96 heads, fp32 state of 3.2 GB updated in place).
 Inputs are synthetic, seeded, and resident in device memory before timing.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--capacity]
 
 Prints one JSON line.  `value` is prefill tokens/s; decode state-update
 bandwidth is reported under "decode"; the gated entry points, the output
@@ -253,6 +253,21 @@ def time_prologue(args, dev, stream, ki, lib):
                       "prefill and the 512 x 96 decode"}
 
 
+def time_capacity(args, dev, stream, ki, prefill):
+    """The capacity run: one sequence of T = 1,048,576 tokens, H = 96, d = 128,
+    bf16, log-decay U[-5, -3] (about 150 GB of inputs and outputs resident)."""
+    import torch
+    x = ki.workload_inputs("long_1m", device=dev)
+    T = x.q.shape[0]
+    o = torch.empty_like(x.v)
+    fin = torch.empty_like(x.init_state)
+    ms = _timed(args, stream, lambda: prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state, None, o=o,
+                                              final_state=fin), max(1, min(args.steps, 3)))
+    byts = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * H * STATE_BYTES
+    return {"tokens": T, "ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "gbps": round(byts / (ms * 1e-3) / 1e9, 1), "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
     """The gated entry points (decay / write-strength logits mapped in-kernel) on the
     same 64K prefill and 512 x 96 decode shapes, timed outside the headline step."""
@@ -294,6 +309,8 @@ def main():
     ap.add_argument("--no-gated", action="store_true", help="skip the timing of the gated entry points")
     ap.add_argument("--no-epilogue", action="store_true",
                     help="skip the timing of the output epilogue and the input prologue")
+    ap.add_argument("--capacity", action="store_true",
+                    help="also time the 1,048,576-token prefill (about 150 GB of device memory)")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (counter calibration)")
     args = ap.parse_args()
@@ -403,6 +420,9 @@ def main():
         res["epilogue"] = time_epilogue(args, dev, stream, ki, lib)
         torch.cuda.empty_cache()
         res["prologue"] = time_prologue(args, dev, stream, ki, lib)
+    if args.capacity:
+        torch.cuda.empty_cache()
+        res["capacity"] = time_capacity(args, dev, stream, ki, kda_chunk_prefill)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)
