@@ -300,6 +300,150 @@ def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
                       "~ N(0, 1); same shapes as the headline step"}
 
 
+# Algorithmic bytes (read, written) per launch of each counted kernel, as bench.py runs it.
+_ROWS = T_PREFILL * H
+_PAIRS = N_DECODE * H
+ALG_BYTES = {
+    "prefill": (_ROWS * (3 * D * 2 + D * 4 + 4) + H * STATE_BYTES, _ROWS * D * 2 + H * STATE_BYTES),
+    "prefill_gated": (_ROWS * (3 * D * 2 + D * 2 + 4) + H * STATE_BYTES, _ROWS * D * 2 + H * STATE_BYTES),
+    "decode": (_PAIRS * (STATE_BYTES + 3 * D * 2 + D * 4 + 4), _PAIRS * (STATE_BYTES + D * 2)),
+    "decode_epilogue": (_PAIRS * (STATE_BYTES + 3 * D * 2 + D * 2 + 4 + D * 2), _PAIRS * (STATE_BYTES + D * 2)),
+    "decode_fused": (_PAIRS * (STATE_BYTES + 3 * D * 2 + 3 * CONV_C * 2 + D * 2 + 4 + D * 2) + H * CONV_C * 16,
+                     _PAIRS * (STATE_BYTES + D * 2 + 3 * CONV_C * 2)),
+    "epilogue": (_ROWS * D * 2 * 2 + D * 4, _ROWS * D * 2),
+    "epilogue_after_prefill": (_ROWS * D * 2 * 2 + D * 4, _ROWS * D * 2),
+    "prologue": (_ROWS * 3 * D * 2 + H * 3 * CONV_C * 2 + H * CONV_C * 16, _ROWS * 3 * D * 2 + H * 3 * CONV_C * 2),
+}
+# Source group (for the code digest) of each counted kernel.
+_LABEL_SOURCE = {"prefill": "prefill", "prefill_gated": "prefill", "decode": "decode",
+                 "decode_epilogue": "decode", "decode_fused": "decode", "epilogue": "epilogue",
+                 "epilogue_after_prefill": "epilogue", "prologue": "prologue"}
+
+
+def _read_dispatches(path):
+    """[(kernel name, {counter: value summed over instances})] in dispatch order, from a rocprofv3
+    results DB or its counter_collection.csv."""
+    if path.endswith(".csv"):
+        import csv
+        acc = {}
+        with open(path, newline="") as fh:
+            for r in csv.DictReader(fh):
+                key = (int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"])
+                acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        rows = sorted((d, n, c, v) for (d, n, c), v in acc.items())
+    else:
+        import sqlite3
+        con = sqlite3.connect(path)
+        rows = con.execute("SELECT dispatch_id, kernel_name, counter_name, SUM(value) FROM counters_collection "
+                           "GROUP BY dispatch_id, counter_name ORDER BY dispatch_id").fetchall()
+        con.close()
+    out, idx = [], {}
+    for disp, name, counter, value in rows:
+        if disp not in idx:
+            idx[disp] = len(out)
+            out.append((name, {}))
+        out[idx[disp]][1][counter] = value
+    return out
+
+
+def _label_dispatches(disp):
+    """Name each dispatch of a `bench.py --no-gated` run after the kernel and the step it belongs to:
+    a prologue followed by a gated prefill is part of the timed layer (not labelled), and an epilogue
+    directly after a gated prefill is the gated prefill's epilogue."""
+    import re
+    names = [d[0] for d in disp]
+    labels = []
+    for i, n in enumerate(names):
+        m = re.search(r"prefill_kernel<[^,]+, 128, 128, (true|false)>", n)
+        d = re.search(r"decode_kernel<[^,]+, 128, 128, (true|false), (true|false), (true|false), \d+>", n)
+        prev_gp = i > 0 and re.search(r"prefill_kernel<[^>]*true>", names[i - 1]) is not None
+        j = i + 1   # the prologue entry point also launches a small kernel for the convolution state
+        while j < len(names) and "prologue_empty_kernel" in names[j]:
+            j += 1
+        next_gp = j < len(names) and re.search(r"prefill_kernel<[^>]*true>", names[j]) is not None
+        if m:
+            labels.append("prefill_gated" if m.group(1) == "true" else "prefill")
+        elif d:
+            gated, norm, pro = (g == "true" for g in d.groups())
+            labels.append("decode_fused" if pro else "decode_epilogue" if norm else
+                          None if gated else "decode")
+        elif "gate_rmsnorm_kernel" in n:
+            labels.append("epilogue_after_prefill" if prev_gp else "epilogue")
+        elif "prologue_kernel" in n:
+            labels.append(None if next_gp else "prologue")
+        else:
+            labels.append(None)
+    return labels
+
+
+def record_counters(pmc_dir: str, copy_gib: float):
+    """Build profiles/hbm_traffic.json from three rocprofv3 runs of
+    `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-gated --calibrate-copy-gib G` stored under
+    pmc_dir/fetch (--pmc FETCH_SIZE), pmc_dir/write (--pmc WRITE_SIZE) and pmc_dir/util
+    (--pmc MfmaUtil VALUBusy), each a results DB or --output-format csv.  HBM bytes are the counters scaled by what they read for the plain
+    copy of G GiB; every record carries the code digest of its kernel's sources."""
+    import glob
+    dbs = {}
+    for part in ("fetch", "write", "util"):
+        found = sorted(glob.glob(os.path.join(pmc_dir, part, "**", "*_results.db"), recursive=True) +
+                       glob.glob(os.path.join(pmc_dir, part, "**", "*counter_collection.csv"), recursive=True))
+        if not found:
+            raise SystemExit(f"no rocprofv3 results under {os.path.join(pmc_dir, part)}")
+        dbs[part] = _read_dispatches(found[0])
+    copy_kib = copy_gib * (1 << 30) / 1024
+
+    # The calibration copy is the one dispatch that writes about G GiB (WRITE_SIZE counts bytes
+    # written one to one); the three runs dispatch the same kernels in the same order.
+    wr = [c.get("WRITE_SIZE", 0.0) for _, c in dbs["write"]]
+    idx = [i for i, v in enumerate(wr) if 0.9 * copy_kib < v < 1.1 * copy_kib]
+    if len(idx) != 1 or len(dbs["fetch"]) != len(dbs["write"]) or \
+            dbs["fetch"][idx[0]][0] != dbs["write"][idx[0]][0]:
+        raise SystemExit("cannot identify the calibration copy in the counter runs")
+    write_factor = wr[idx[0]] / copy_kib
+    fetch_factor = dbs["fetch"][idx[0]][1]["FETCH_SIZE"] / copy_kib
+    per = {}
+    for part, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"), ("util", "MfmaUtil"),
+                          ("util", "VALUBusy")):
+        disp = dbs[part]
+        for lab, (_, c) in zip(_label_dispatches(disp), disp):
+            if lab is not None and counter in c:
+                per.setdefault(lab, {}).setdefault(counter, []).append(c[counter])
+    rec = {}
+    for lab, vals in per.items():
+        src = _LABEL_SOURCE[lab]
+        f, w = vals.get("FETCH_SIZE", []), vals.get("WRITE_SIZE", [])
+        if not f or not w:
+            continue
+        rd = sum(f) / len(f) * 1024 / fetch_factor
+        wr = sum(w) / len(w) * 1024 / write_factor
+        alg_r, alg_w = ALG_BYTES[lab]
+        mu, vb = vals.get("MfmaUtil", []), vals.get("VALUBusy", [])
+        rec[lab] = {"source": KERNEL_SOURCES[src][0], "code_digest": kernel_digest(src),
+                    "hbm_bytes_read": rd, "hbm_bytes_written": wr, "alg_bytes_read": alg_r,
+                    "alg_bytes_written": alg_w, "fetch_kib_raw": f, "write_kib_raw": w,
+                    "mfma_util_pct": sum(mu) / len(mu) if mu else None,
+                    "valu_busy_pct": sum(vb) / len(vb) if vb else None}
+    rec["calibration"] = {"fetch_factor": fetch_factor, "write_factor": write_factor,
+                          "copy_bytes": int(copy_gib * (1 << 30))}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(f"calibration: FETCH_SIZE factor {fetch_factor:.4f}, WRITE_SIZE factor {write_factor:.4f} "
+          f"(copy of {copy_gib:g} GiB)")
+    print(f"{'kernel (per dispatch, mean)':28s} {'GB read':>8s} {'GB wrtn':>8s} {'alg rd':>8s} {'alg wr':>8s}  "
+          f"measured / algorithmic   MfmaUtil %  VALUBusy %")
+    for lab, r in rec.items():
+        if lab == "calibration":
+            continue
+        mu = "-" if r["mfma_util_pct"] is None else f"{r['mfma_util_pct']:.1f}"
+        vb = "-" if r["valu_busy_pct"] is None else f"{r['valu_busy_pct']:.1f}"
+        print(f"{lab:28s} {r['hbm_bytes_read'] / 1e9:8.3f} {r['hbm_bytes_written'] / 1e9:8.3f} "
+              f"{r['alg_bytes_read'] / 1e9:8.3f} {r['alg_bytes_written'] / 1e9:8.3f}  "
+              f"{r['hbm_bytes_read'] / r['alg_bytes_read']:.2f}x / {r['hbm_bytes_written'] / r['alg_bytes_written']:.2f}x"
+              f"          {mu:>6s}      {vb:>6s}")
+    print(f"wrote {os.path.relpath(path, ROOT)}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,7 +457,13 @@ def main():
                     help="also time the 1,048,576-token prefill (about 150 GB of device memory)")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (counter calibration)")
+    ap.add_argument("--record-counters", metavar="PMC_DIR",
+                    help="no GPU run: build profiles/hbm_traffic.json from the rocprofv3 passes under PMC_DIR "
+                         "(fetch/, write/, util/) of a run made with --calibrate-copy-gib")
     args = ap.parse_args()
+    if args.record_counters:
+        record_counters(args.record_counters, args.calibrate_copy_gib or 4.0)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
                                    "this build (--gpus must be 1)"}))

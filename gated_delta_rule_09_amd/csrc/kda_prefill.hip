@@ -894,13 +894,12 @@ template <typename T, int DK, int DV, bool GATED>
 hipError_t launch_t(const PrefillArgs& a) {
     using PL = Plan<T, DK>;
     auto kern = prefill_kernel<T, DK, DV, GATED>;
-    static bool attr_set = false;   // per instantiation; the attribute is a property of the function
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, PL::TOTAL);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // The dynamic-LDS limit is set on every launch: it is a host-side property of
+    // the function on the current device, cheap to set, and no cached flag can
+    // then miss a second device or race between threads.
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       PL::TOTAL);
+    if (e != hipSuccess) return e;
     const int64_t units = (int64_t)a.N * a.H;
     constexpr int NV = DV / kBV;
     const int64_t blocks = NV == 2 ? 16 * ((units + 7) / 8) : units;
