@@ -465,8 +465,8 @@ def main():
         record_counters(args.record_counters, args.calibrate_copy_gib or 4.0)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
-                                   "this build (--gpus must be 1)"}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the library's path is single-GPU "
+                                   "(--gpus must be 1)"}))
         sys.exit(2)
 
     import torch

@@ -3,7 +3,7 @@
     python -m gated_delta_rule_09_amd.build          # or build() from Python
 
 Always recompiles.  The library lands next to this file so that the test
-suite, the benchmark and a GPU machine running from a copy of the tree load the
+suite, the benchmark and any machine running from a copy of the tree load the
 same file.
 """
 import os
