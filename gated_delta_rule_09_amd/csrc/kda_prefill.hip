@@ -2,8 +2,8 @@
 //
 // The recurrence of "Kimi K3 -- Architecture Notes", section 1.1,
 //     S_t = (I - b_t k_t k_t^T) Diag(alpha_t) S_{t-1} + b_t k_t v_t^T,  o_t = S_t^T q_t,
-// is evaluated "recurrent across chunks and parallel within each chunk"
-// (section 1.2).  Tokens are streamed in chunks of 64, and each chunk is cut
+// is evaluated chunkwise as section 1.2 describes it: the state is carried
+// serially from chunk to chunk, and the work inside a chunk is parallel.  Tokens are streamed in chunks of 64, and each chunk is cut
 // into four 16-token tiles ("secondary tiles", section 1.2).  The state is
 // carried from tile to tile.  For one tile of positions r = 1..16 starting from
 // state S (d_k x d_v), with x_r = sum_{s<=r} log2-decay (per key channel),

@@ -1,8 +1,9 @@
 """The tile algebra of the chunkwise prefill, checked in fp64 against the oracle's token loop.
 
-"Kimi K3 -- Architecture Notes", section 1.2, evaluates KDA "recurrent across chunks and parallel
-within each chunk", with 16-token secondary tiles whose decay factors are taken relative to a
-reference point inside the tile, so that a lower bound on log alpha keeps every factor in range.
+"Kimi K3 -- Architecture Notes", section 1.2, evaluates KDA chunk by chunk: the state is carried
+serially across chunks and the work inside a chunk is parallel.  It uses 16-token secondary tiles
+whose decay factors are taken relative to a reference point inside the tile, so that a lower
+bound on log alpha keeps every factor in range.
 The prefill kernel carries the state from tile to tile.  For one tile of positions r = 1..L
 (L <= 16) starting from state S, with x_r the inclusive prefix sum of log2(alpha) over the tile
 (per key channel) and X = x_L:
