@@ -13,7 +13,7 @@ head of KDA as the recurrence
     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
     o_t = S_t^T q_t
 
-with the state S in R^{d_k x d_v} (same section: "fixed size"), alpha_t a
+with the state S in R^{d_k x d_v} (constant in size, per the same section), alpha_t a
 per-channel retention factor in (0,1)^{d_k} and beta_t a scalar write strength.
 The oracle evaluates that definition literally, one token at a time, in fp64,
 with alpha_t = exp(log_alpha_t) (the same notes, section 1.2, parameterise the
