@@ -53,6 +53,12 @@ SIGNATURES = {
                                                 ctypes.c_int, _VP, _VP, _VP, _VP, _VP]),
     "kda_decode_step_fused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _VP,
                                               _I32, _I32, _I32, _I32, ctypes.c_int, _VP, _VP]),
+    "kda_chunk_prefill_split": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, ctypes.c_int,
+                                                _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
+    "kda_chunk_prefill_gated_split": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32,
+                                                      ctypes.c_int, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
+    "kda_split_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32, ctypes.c_int, _I32]),
+    "kda_split_segments": (_I32, [_I64, _I32, _I32, _I32, _I32]),
 }
 
 _lib = None
@@ -222,6 +228,94 @@ def kda_chunk_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != KDA_OK:
         raise KDAError("kda_chunk_prefill_gated", st)
     return o, final_state
+
+
+def split_segments(total_T: int, H: int, d_k: int, d_v: int, num_cus: Optional[int] = None,
+                   device: Optional[torch.device] = None) -> int:
+    """Segment count for the time-split prefill (include/kda.h, kda_split_segments).
+    num_cus defaults to the compute units of ``device`` (the current device)."""
+    lib = load()
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
+    return int(lib.kda_split_segments(int(total_T), int(H), int(d_k), int(d_v), int(num_cus)))
+
+
+def split_workspace_bytes(total_T: int, H: int, d_k: int, d_v: int, dtype: torch.dtype, segments: int) -> int:
+    """Workspace bytes of a time-split prefill (include/kda.h, kda_split_workspace_bytes)."""
+    return int(load().kda_split_workspace_bytes(int(total_T), int(H), int(d_k), int(d_v), _dtype_code(dtype),
+                                                int(segments)))
+
+
+def _split_call(name: str, q, k, v, decay, decay_dtype, a_log, beta, init_state, segments, workspace, o,
+                final_state, output_final_state):
+    lib = load()
+    T, H, d_k = q.shape
+    d_v = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(dt)
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(k, "k", (T, H, d_k), dt, dev)
+    _check(v, "v", (T, H, d_v), dt, dev)
+    _check(decay, "decay", (T, H, d_k), decay_dtype, dev)
+    if a_log is not None:
+        _check(a_log, "a_log", (H,), torch.float32, dev)
+    _check(beta, "beta", (T, H), torch.float32, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (1, H, d_k, d_v), torch.float32, dev)
+    if segments is None:
+        segments = split_segments(T, H, d_k, d_v, device=dev)
+    if o is None:
+        o = torch.empty((T, H, d_v), dtype=dt, device=dev)
+    _check(o, "o", (T, H, d_v), dt, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((1, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check(final_state, "final_state", (1, H, d_k, d_v), torch.float32, dev)
+    need = int(lib.kda_split_workspace_bytes(T, H, d_k, d_v, code, int(segments)))
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None and workspace.device != dev:
+        raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(decay)]
+    if a_log is not None:
+        args.append(_ptr(a_log))
+    args += [_ptr(beta), _ptr(init_state), T, H, d_k, d_v, code, int(segments), _ptr(workspace), ws_bytes,
+             _ptr(o), _ptr(final_state), _stream_handle(dev)]
+    st = getattr(lib, name)(*args)
+    if st != KDA_OK:
+        raise KDAError(name, st)
+    return o, final_state
+
+
+def kda_chunk_prefill_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            log_alpha: torch.Tensor, beta: torch.Tensor,
+                            init_state: Optional[torch.Tensor] = None,
+                            segments: Optional[int] = None,
+                            workspace: Optional[torch.Tensor] = None,
+                            o: Optional[torch.Tensor] = None,
+                            final_state: Optional[torch.Tensor] = None,
+                            output_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Prefill of one sequence split in time (include/kda.h, kda_chunk_prefill_split).
+    segments=None asks the library's cost model for the device; the workspace is
+    allocated here unless given (a device tensor of at least split_workspace_bytes
+    bytes).  Returns (o, final_state) with final_state [1, H, d_k, d_v]."""
+    return _split_call("kda_chunk_prefill_split", q, k, v, log_alpha, torch.float32, None, beta, init_state,
+                       segments, workspace, o, final_state, output_final_state)
+
+
+def kda_chunk_prefill_gated_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  g_logits: torch.Tensor, a_log: torch.Tensor, beta_logits: torch.Tensor,
+                                  init_state: Optional[torch.Tensor] = None,
+                                  segments: Optional[int] = None,
+                                  workspace: Optional[torch.Tensor] = None,
+                                  o: Optional[torch.Tensor] = None,
+                                  final_state: Optional[torch.Tensor] = None,
+                                  output_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated prefill of one sequence split in time (include/kda.h, kda_chunk_prefill_gated_split)."""
+    return _split_call("kda_chunk_prefill_gated_split", q, k, v, g_logits, q.dtype, a_log, beta_logits, init_state,
+                       segments, workspace, o, final_state, output_final_state)
 
 
 def kda_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -2,6 +2,7 @@
 // Every validation failure returns before any HIP runtime call.
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <math.h>
 #include <string.h>
@@ -141,6 +142,78 @@ kda_status prefill_impl(const char* name, const void* q, const void* k, const vo
     return KDA_OK;
 }
 
+// ---- Time split of one sequence ------------------------------------------
+constexpr int64_t kChunkTokens = 64;   // the prefill kernel's chunk
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Segments of a whole number of chunks: the requested count sets the segment
+// length, and that length fixes how many segments there are (never more than
+// requested; one when the sequence has at most one chunk).  Workspace: the
+// segment end states, the transitions of segments 1.., and Phi_t^T q_t of
+// tokens seg_len.., each at a 256-byte boundary.
+struct SplitPlan {
+    int32_t segments = 1;
+    int64_t seg_len = 0;
+    size_t phis = 0, qt = 0, bytes = 0;    // offsets (the end states start at 0) and total
+};
+
+SplitPlan split_plan(int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, int32_t segments) {
+    SplitPlan p;
+    const int64_t chunks = (total_T + kChunkTokens - 1) / kChunkTokens;
+    if (chunks <= 1 || segments <= 1) return p;
+    const int64_t per = (chunks + segments - 1) / segments;
+    const int32_t n = (int32_t)((chunks + per - 1) / per);
+    if (n <= 1) return p;
+    p.segments = n;
+    p.seg_len = per * kChunkTokens;
+    const size_t es = dtype == KDA_BF16 ? 2 : 4;
+    p.phis = round256((size_t)n * H * d_k * d_v * 4);
+    p.qt = p.phis + round256((size_t)(n - 1) * H * d_k * d_k * 4);
+    p.bytes = p.qt + round256((size_t)(total_T - p.seg_len) * H * d_k * es);
+    return p;
+}
+
+kda_status split_impl(const char* name, const void* q, const void* k, const void* v, const void* decay,
+                      const float* beta, const float* a_log, bool gated, const float* init_state, int64_t total_T,
+                      int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, int32_t segments, void* workspace,
+                      size_t workspace_bytes, void* o, float* final_state, void* stream) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (segments < 1) return KDA_ERR_VALUE;
+    if (H < 1 || H > 65535 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
+    if (dtype == KDA_F32 && d_k != 64) return KDA_ERR_SHAPE;
+    const SplitPlan p = split_plan(total_T, H, d_k, d_v, dtype, segments);
+    if (p.segments == 1)
+        return prefill_impl(name, q, k, v, decay, beta, a_log, gated, init_state, nullptr, 1, total_T, H, d_k, d_v,
+                            dtype, o, final_state, stream);
+    if ((int64_t)p.segments * H > (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
+    // The correction addresses 256 tokens of a head with 32-bit byte offsets,
+    // and its grid has one workgroup per (head, 256 tokens of a segment).
+    const int64_t es = dtype == KDA_BF16 ? 2 : 4;
+    if (256 * (int64_t)H * (d_k > d_v ? d_k : d_v) * es > (int64_t)INT32_MAX) return KDA_ERR_SHAPE;
+    if ((int64_t)H * (p.segments - 1) * ((p.seg_len + 255) / 256) > (int64_t)INT32_MAX) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !decay || !beta || !o || (gated && !a_log) || !workspace) return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, decay, beta, a_log, init_state, o, final_state, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGN;
+    if (workspace_bytes < p.bytes) return KDA_ERR_VALUE;
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    kda::PrefillArgs a{q, k, v, decay, beta, init_state, nullptr, 1, total_T, H, d_k, d_v,
+                       dtype == KDA_BF16, o, final_state, reinterpret_cast<hipStream_t>(stream), gated, a_log};
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const kda::SplitWork w{p.segments, p.seg_len, reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + p.phis),
+                           ws + p.qt};
+    hipError_t e = kda::launch_prefill_split_runs(a, w);
+    if (e == hipSuccess) e = kda::launch_split_scan(a, w);
+    if (e == hipSuccess) e = kda::launch_split_correct(a, w);
+    if (e != hipSuccess) {
+        set_error(name, e);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
 kda_status epilogue_checks(const void* o, const void* gate, const float* weight, int64_t rows, int32_t d_v,
                            float eps, kda_dtype dtype, const void* y) {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
@@ -204,6 +277,62 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v,
                                    void* o, float* final_state, void* stream) {
     return prefill_impl("kda_chunk_prefill_gated launch", q, k, v, g_logits, beta_logits, a_log, true, init_state,
                         cu_seqlens, N, total_T, H, d_k, d_v, dtype, o, final_state, stream);
+}
+
+int32_t kda_split_segments(int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, int32_t num_cus) {
+    if (total_T <= 0 || H < 1 || H > 65535 || !supported_d(d_k) || !supported_d(d_v) || num_cus < 1) return 1;
+    const int64_t chunks = (total_T + kChunkTokens - 1) / kChunkTokens;
+    // Workgroups of a job of `units` (sequence, head) pairs at `cols` value
+    // columns: one per 64 columns, padded to groups of 16 for 128 columns.
+    auto wgs = [](int64_t units, int32_t cols) { return cols == 128 ? 16 * ((units + 7) / 8) : units; };
+    auto rounds = [&](int64_t w) { return (w + num_cus - 1) / num_cus; };
+    // Cost in chunk steps of one workgroup (one workgroup per CU).  The segment
+    // runs take rounds x (chunks per segment); with d_v = d_k both jobs share
+    // one launch.  Each scan step costs about one chunk step, and the
+    // correction streams qt and o once more: about 2 (d_k + 2 d_v) bytes per
+    // token-head at some 5 TB/s, against about 3 us per chunk step.
+    double best = (double)rounds(wgs(H, d_v)) * chunks;
+    int32_t best_n = 1;
+    for (int64_t n = 2; n <= 256 && n <= chunks; ++n) {
+        const int64_t per = (chunks + n - 1) / n;
+        if ((chunks + per - 1) / per != n) continue;    // this count is not reachable
+        const int64_t run = wgs(n * H, d_v), trans = wgs((n - 1) * H, d_k);
+        const int64_t r = d_v == d_k ? rounds(run + trans) : rounds(run) + rounds(trans);
+        const double corr = (double)(total_T - per * kChunkTokens) * H * (d_k + 2 * d_v) * 2.0 / 5e12 / 3e-6;
+        const double cost = (double)r * per + (double)(n - 1) + corr;
+        if (cost < best * 0.95) {      // a split must gain at least 5%
+            best = cost;
+            best_n = (int32_t)n;
+        }
+    }
+    return best_n;
+}
+
+size_t kda_split_workspace_bytes(int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                 int32_t segments) {
+    if (total_T < 0 || H < 1 || !supported_d(d_k) || !supported_d(d_v) || (dtype != KDA_F32 && dtype != KDA_BF16))
+        return 0;
+    return split_plan(total_T, H, d_k, d_v, dtype, segments).bytes;
+}
+
+kda_status kda_chunk_prefill_split(const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta, const float* init_state,
+                                   int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                   int32_t segments, void* workspace, size_t workspace_bytes,
+                                   void* o, float* final_state, void* stream) {
+    return split_impl("kda_chunk_prefill_split launch", q, k, v, log_alpha, beta, nullptr, false, init_state,
+                      total_T, H, d_k, d_v, dtype, segments, workspace, workspace_bytes, o, final_state, stream);
+}
+
+kda_status kda_chunk_prefill_gated_split(const void* q, const void* k, const void* v,
+                                         const void* g_logits, const float* a_log, const float* beta_logits,
+                                         const float* init_state, int64_t total_T, int32_t H,
+                                         int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                         int32_t segments, void* workspace, size_t workspace_bytes,
+                                         void* o, float* final_state, void* stream) {
+    return split_impl("kda_chunk_prefill_gated_split launch", q, k, v, g_logits, beta_logits, a_log, true,
+                      init_state, total_T, H, d_k, d_v, dtype, segments, workspace, workspace_bytes, o,
+                      final_state, stream);
 }
 
 kda_status kda_output_gate_rmsnorm(const void* o, const void* gate_logits, const float* norm_weight,

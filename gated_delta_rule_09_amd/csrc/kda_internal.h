@@ -44,6 +44,33 @@ struct PrefillArgs {
     const float* a_log = nullptr;
 };
 
+// One job of a prefill launch (a kernel argument): a set of sequences over the
+// launch's q, k, decay and beta, with its own values, states and outputs.
+enum : int32_t { kInitAll = 0, kInitFirst = 1, kInitIdentity = 2 };
+struct PrefillJob {
+    const void* v;               // [T, H, d_v]; null: every value is zero
+    const float* init_state;     // kInitAll: [N, H, d_k, d_v]; kInitFirst: sequence 0 only; null: zeros
+    const int32_t* cu_seqlens;   // sequence offsets; null: uniform segments (seg_len > 0) or all tokens
+    void* o;                     // outputs; its first row holds token o_row0
+    float* final_state;          // [N, H, d_k, d_v] end states; may be null
+    int64_t seg_len;             // sequence n covers [(n + n_off) seg_len, + seg_len) clipped to T
+    int64_t o_row0;
+    int32_t n_off;
+    int32_t units;               // N * H
+    int32_t blocks;              // workgroups (set by the launcher)
+    int32_t init_mode;           // kInitAll, kInitFirst (state of sequence 0 only), kInitIdentity (d_v = d_k)
+};
+
+// Time-split workspace of one sequence cut into `segments` runs of seg_len
+// tokens (a multiple of the 64-token chunk).
+struct SplitWork {
+    int32_t segments;
+    int64_t seg_len;
+    float* ends;     // [segments, H, d_k, d_v] fp32: end state of each segment
+    float* phis;     // [segments - 1, H, d_k, d_k] fp32: transition of segments 1..
+    void* qt;        // [T - seg_len, H, d_k] element type: Phi_t^T q_t of tokens seg_len..T-1
+};
+
 // y = Sigmoid(gate) * weight * o / sqrt(mean(o^2) + eps) over rows of d_v
 // values; weight may be null (ones); y may alias o or gate.
 struct EpilogueArgs {
@@ -75,5 +102,10 @@ bool prologue_grid_fits(int64_t total_T, int32_t H);
 hipError_t launch_epilogue(const EpilogueArgs& a);
 int64_t epilogue_max_rows();
 hipError_t launch_prefill(const PrefillArgs& a);
+// Time split of one sequence (N = 1): the segment runs, then the serial scan
+// over segment end states, then the output correction.
+hipError_t launch_prefill_split_runs(const PrefillArgs& a, const SplitWork& w);
+hipError_t launch_split_scan(const PrefillArgs& a, const SplitWork& w);
+hipError_t launch_split_correct(const PrefillArgs& a, const SplitWork& w);
 
 }  // namespace kda

@@ -402,15 +402,26 @@ struct Plan {
 // (Kimi K3 row of its table), g = -5 Sigmoid(e^{A_h} z), beta = Sigmoid(logit),
 // is applied on the fly.  Otherwise `decay` holds log alpha (fp32) and `beta`
 // beta.
+//
+// A launch runs one or two jobs over the same q, k, decay and beta (the
+// workgroups of j1 follow those of j0); each job is a set of sequences with
+// their own values, initial states and outputs (PrefillJob).
 template <typename T, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ q, const T* __restrict__ k,
     const void* __restrict__ decay, const float* __restrict__ beta, const float* __restrict__ a_log,
-    const float* __restrict__ init_state, const int32_t* __restrict__ cu_seqlens,
-    int64_t total_T, int H, int units, T* __restrict__ o, float* __restrict__ final_state) {
+    int64_t total_T, int H, PrefillJob j0, PrefillJob j1) {
     // Decay input: fp32 log alpha, or decay logits of type T (GATED).
     using DT = typename std::conditional<GATED, T, float>::type;
     const DT* log_alpha = reinterpret_cast<const DT*>(decay);
+    const bool second = (int)blockIdx.x >= j0.blocks;
+    const PrefillJob& J = second ? j1 : j0;
+    const T* __restrict__ v = reinterpret_cast<const T*>(J.v);
+    const float* __restrict__ init_state = J.init_state;
+    const int32_t* __restrict__ cu_seqlens = J.cu_seqlens;
+    T* __restrict__ o = reinterpret_cast<T*>(J.o);
+    float* __restrict__ final_state = J.final_state;
+    const int units = J.units;
     using OT = T;
     using OP = Op<OT>;
     using PL = Plan<OT, DK>;
@@ -429,7 +440,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
 
     // Workgroup -> (unit = sequence * H + head, value block).  With two value
     // blocks, the pair of a unit sits 8 workgroups apart (same XCD).
-    const int lid = blockIdx.x;
+    const int lid = (int)blockIdx.x - (second ? j0.blocks : 0);
     int unit, vblk;
     if constexpr (NV == 2) {
         unit = 8 * (lid >> 4) + (lid & 7);
@@ -457,14 +468,18 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     const int cb = (lane % LPR) * CPL;           // SI: first key channel of this lane
     const int pg = lane / LPR;                   // SI: position group (positions RP pg .. RP pg + RP - 1)
 
-    // Sequence range, clamped so malformed offsets cannot address out of range.
+    // Sequence range, clamped so malformed offsets cannot address out of range:
+    // from the offsets, or segment n + n_off of seg_len tokens, or every token.
     int64_t seq0 = 0, seq1 = total_T;
     if (cu_seqlens != nullptr) {
         seq0 = cu_seqlens[n];
         seq1 = cu_seqlens[n + 1];
-        seq0 = seq0 < 0 ? 0 : (seq0 > total_T ? total_T : seq0);
-        seq1 = seq1 < seq0 ? seq0 : (seq1 > total_T ? total_T : seq1);
+    } else if (J.seg_len > 0) {
+        seq0 = (int64_t)(n + J.n_off) * J.seg_len;
+        seq1 = seq0 + J.seg_len;
     }
+    seq0 = seq0 < 0 ? 0 : (seq0 > total_T ? total_T : seq0);
+    seq1 = seq1 < seq0 ? seq0 : (seq1 > total_T ? total_T : seq1);
     const int64_t len = seq1 - seq0;
     const int64_t nchunks = (len + kC - 1) / kC;
 
@@ -525,8 +540,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         beta_r = __uint_as_float(buf_ld32(make_rsrc(beta + row_of(c), valid_rows(c) * 4),
                                           (16 * wave + l16) * (uint32_t)H * 4));
     };
+    // No values (v null): an empty range, so every value reads as zero.
     auto v_rsrc = [&](int64_t c) {
-        return make_rsrc(v + row_of(c) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)));
+        return v != nullptr ? make_rsrc(v + row_of(c) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)))
+                            : make_rsrc(nullptr, 0u);
     };
     auto load_v_tile = [&](Rsrc rv, int i) {
         const uint32_t rs = (uint32_t)H * DV;
@@ -759,7 +776,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         const OT* sPD = reinterpret_cast<const OT*>(buf + PL::PD);
         const OT* sAD = reinterpret_cast<const OT*>(buf + PL::AD);
         const float* sDEC = reinterpret_cast<const float*>(buf + PL::DEC);
-        const Rsrc ro = make_rsrc(o + row_of(c) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)));
+        const Rsrc ro = make_rsrc(o + (row_of(c) - J.o_row0 * H) * DV + vcol, valid_rows(c) * (DV * (uint32_t)sizeof(T)));
         inverse(c, wave - kSIW);
         // LDS operands of one tile (A excepted: it is read after its flag).
         // Tile decay of the state rows 16 ct + 4 lg + e: the 4 NCT values a
@@ -866,7 +883,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         for (int ct = 0; ct < NCT; ++ct)
     #pragma unroll
             for (int e = 0; e < 4; ++e)
-                Sacc[ct][e] = init_state ? init_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] : 0.f;
+                Sacc[ct][e] = J.init_mode == kInitIdentity ? (16 * ct + 4 * lg + e == vcol + l16 ? 1.f : 0.f)
+                              : (init_state != nullptr && (J.init_mode == kInitAll || n == 0))
+                                  ? init_state[sbase + (int64_t)(16 * ct + 4 * lg + e) * DV + vcol + l16] : 0.f;
         if (wave == kSIW && lane < kTiles) __hip_atomic_store(sFLAG + lane, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (nchunks > 0) {
             {
@@ -890,8 +909,16 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     }
 }
 
+// Workgroups of a job: with two value blocks, the pair of a unit sits 8
+// workgroups apart (the grid is padded to whole groups of 16).
+template <int DV>
+int64_t job_blocks(int64_t units) {
+    return DV / kBV == 2 ? 16 * ((units + 7) / 8) : units;
+}
+
+// One launch of the jobs j0 and j1 (j1.units may be 0).
 template <typename T, int DK, int DV, bool GATED>
-hipError_t launch_t(const PrefillArgs& a) {
+hipError_t launch_jobs(const PrefillArgs& a, PrefillJob j0, PrefillJob j1) {
     using PL = Plan<T, DK>;
     auto kern = prefill_kernel<T, DK, DV, GATED>;
     // The dynamic-LDS limit is set on every launch: it is a host-side property of
@@ -900,13 +927,41 @@ hipError_t launch_t(const PrefillArgs& a) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        PL::TOTAL);
     if (e != hipSuccess) return e;
-    const int64_t units = (int64_t)a.N * a.H;
-    constexpr int NV = DV / kBV;
-    const int64_t blocks = NV == 2 ? 16 * ((units + 7) / 8) : units;
+    j0.blocks = (int32_t)job_blocks<DV>(j0.units);
+    j1.blocks = (int32_t)job_blocks<DV>(j1.units);
+    const int64_t blocks = (int64_t)j0.blocks + j1.blocks;
+    if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kNW), PL::TOTAL, a.stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha, a.beta, a.a_log,
-                       a.init_state, a.cu_seqlens, a.total_T, a.H, (int)units, (T*)a.o, a.final_state);
+                       (const T*)a.q, (const T*)a.k, a.log_alpha, a.beta, a.a_log, a.total_T, a.H, j0, j1);
     return hipGetLastError();
+}
+
+template <typename T, int DK, int DV, bool GATED>
+hipError_t launch_t(const PrefillArgs& a) {
+    PrefillJob j0{a.v, a.init_state, a.cu_seqlens, a.o, a.final_state, 0, 0, 0, a.N * a.H, 0, kInitAll};
+    PrefillJob none{};
+    return launch_jobs<T, DK, DV, GATED>(a, j0, none);
+}
+
+// Time split of one sequence into `segments` runs of seg_len tokens (phase 1):
+// every segment from a zero state (the first from the initial state), giving
+// its outputs in o and its end state in ends[p]; and every segment after the
+// first from the identity with no values (d_k value columns), giving the
+// outputs Phi_t^T q_t in qt (rows from token seg_len on) and its transition
+// in phis[p - 1].  One launch when d_v = d_k, else two.
+template <typename T, int DK, int DV, bool GATED>
+hipError_t launch_split_t(const PrefillArgs& a, const SplitWork& w) {
+    PrefillJob run{a.v, a.init_state, nullptr, a.o, w.ends, w.seg_len, 0, 0, w.segments * a.H, 0, kInitFirst};
+    PrefillJob trans{nullptr, nullptr, nullptr, w.qt, w.phis, w.seg_len, w.seg_len, 1,
+                     (w.segments - 1) * a.H, 0, kInitIdentity};
+    if constexpr (DV == DK) {
+        return launch_jobs<T, DK, DV, GATED>(a, run, trans);
+    } else {
+        PrefillJob none{};
+        hipError_t e = launch_jobs<T, DK, DV, GATED>(a, run, none);
+        if (e != hipSuccess) return e;
+        return launch_jobs<T, DK, DK, GATED>(a, trans, none);
+    }
 }
 
 }  // namespace
@@ -924,6 +979,21 @@ hipError_t launch_prefill_g(const PrefillArgs& a) {
 
 hipError_t launch_prefill(const PrefillArgs& a) {
     return a.gated ? launch_prefill_g<true>(a) : launch_prefill_g<false>(a);
+}
+
+template <bool GATED>
+hipError_t launch_split_g(const PrefillArgs& a, const SplitWork& w) {
+    if (a.bf16) {
+        if (a.d_k == 128)
+            return a.d_v == 128 ? launch_split_t<uint16_t, 128, 128, GATED>(a, w)
+                                : launch_split_t<uint16_t, 128, 64, GATED>(a, w);
+        return a.d_v == 128 ? launch_split_t<uint16_t, 64, 128, GATED>(a, w) : launch_split_t<uint16_t, 64, 64, GATED>(a, w);
+    }
+    return a.d_v == 128 ? launch_split_t<float, 64, 128, GATED>(a, w) : launch_split_t<float, 64, 64, GATED>(a, w);
+}
+
+hipError_t launch_prefill_split_runs(const PrefillArgs& a, const SplitWork& w) {
+    return a.gated ? launch_split_g<true>(a, w) : launch_split_g<false>(a, w);
 }
 
 }  // namespace kda

@@ -1,0 +1,269 @@
+// Time split of one long sequence across the GPU (gfx950): the two passes
+// after the segment runs.
+//
+// The recurrence of "Kimi K3 -- Architecture Notes", section 1.1, is affine
+// in the state: a run of tokens maps S to Phi S + B, where Phi is the product
+// of the step matrices (I - b k k^T) Diag(alpha) and B is the end state from
+// a zero start.  One sequence cut into segments p = 0..P-1 of seg_len tokens
+// is therefore evaluated as
+//   1. every segment at once: from a zero state (segment 0 from the initial
+//      state), giving its outputs o0 and its end state B_p; and every segment
+//      after the first from the identity with no values, giving Phi_p and the
+//      outputs qt_t = Phi_t^T q_t (Phi_t: the product up to token t).  The
+//      prefill kernel runs both (kda_prefill.hip);
+//   2. the serial scan  S_end,p = Phi_p S_end,p-1 + B_p  (split_scan_kernel);
+//   3. the correction  o_t = o0_t + S_end,p-1^T qt_t  for the tokens of
+//      segments p >= 1 (split_correct_kernel).
+//
+// The scan is a chain of small fp32 products (d_k x d_k times d_k x 16 per
+// workgroup and step) on v_mfma_f32_16x16x4_f32.  The correction is a
+// streaming GEMM: bf16 inputs use v_mfma_f32_16x16x32_bf16 with the state
+// split into a bf16 high part and a bf16 remainder (about 16 significant
+// bits), fp32 inputs use the fp32 MFMA.
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Scan.  One workgroup (4 waves) per (head, block of 16 value columns).  The
+// 16 columns of the running state are kept transposed in LDS, ST[j][m] =
+// S[m][c0 + j]; wave w forms row tiles w, w + 4, ... of Phi_p S + B_p.
+// MFMA operands: lane (i = l % 16, g = l / 16) supplies Phi[16 ct + i][16 u +
+// 4 g + e] and ST[i][16 u + 4 g + e] to the products e = 0..3 of K-block u
+// (any assignment of the contraction index to the products is complete, as
+// long as both operands use the same one).  The accumulator then holds row
+// 16 ct + 4 g + e, column c0 + (l % 16) in register e.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void split_scan_kernel(float* __restrict__ ends, const float* __restrict__ phis,
+                                                         float* __restrict__ final_state, int segments, int H) {
+    constexpr int NCT = DK / 16;
+    constexpr int NB = DV / 16;
+    constexpr int LDT = DK + 4;
+    __shared__ __attribute__((aligned(16))) float ST[16 * LDT];
+    const int h = blockIdx.x / NB;
+    const int c0 = 16 * (blockIdx.x % NB);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const size_t slab = (size_t)DK * DV, tslab = (size_t)DK * DK;
+
+    // Start: the end state of segment 0 (the true one).
+    {
+        const float* src = ends + (size_t)h * slab;
+        for (int x = tid; x < DK * 16; x += 256) {
+            const int m = x >> 4, j = x & 15;
+            ST[j * LDT + m] = src[(size_t)m * DV + c0 + j];
+        }
+    }
+    f32x4 cur[(NCT + 3) / 4];
+#pragma unroll
+    for (int r = 0; r < (NCT + 3) / 4; ++r) cur[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 1; p < segments; ++p) {
+        __syncthreads();
+        const float* phi = phis + ((size_t)(p - 1) * H + h) * tslab;
+        float* bp = ends + ((size_t)p * H + h) * slab;
+#pragma unroll
+        for (int r = 0; r < (NCT + 3) / 4; ++r) {
+            const int ct = wave + 4 * r;
+            if (ct >= NCT) break;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < DK / 16; ++u) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(phi + (size_t)(16 * ct + i) * DK + 16 * u + 4 * g);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(ST + i * LDT + 16 * u + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float* dst = bp + (size_t)(16 * ct + 4 * g + e) * DV + c0 + i;
+                acc[e] += *dst;
+                *dst = acc[e];
+            }
+            cur[r] = acc;
+        }
+        __syncthreads();   // every read of ST for step p is done
+#pragma unroll
+        for (int r = 0; r < (NCT + 3) / 4; ++r) {
+            const int ct = wave + 4 * r;
+            if (ct >= NCT) break;
+            *reinterpret_cast<f32x4*>(ST + i * LDT + 16 * ct + 4 * g) = cur[r];
+        }
+    }
+    if (final_state != nullptr) {
+        __syncthreads();
+        for (int x = tid; x < DK * 16; x += 256) {
+            const int m = x >> 4, j = x & 15;
+            final_state[(size_t)h * slab + (size_t)m * DV + c0 + j] = ST[j * LDT + m];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Correction.  One workgroup (4 waves) per (head, segment p >= 1, block of
+// up to 256 tokens of that segment); a wave takes 16 tokens of each 64-token
+// sub-block.  The state that segment p starts from, S = ends[p - 1], is staged
+// transposed in LDS (ST[j][m] = S[m][j]).  The product is formed as
+// D = ST * QT^T, so a lane (n = l % 16, g = l / 16) ends with the correction of
+// token n for the four consecutive value columns 16 ct + 4 g + e.
+// ---------------------------------------------------------------------------
+constexpr int kCorrTok = 256;
+
+template <typename T, int DK, int DV> struct CorrOps;
+
+template <int DK, int DV> struct CorrOps<uint16_t, DK, DV> {
+    static constexpr int LDT = DK + 8;     // bf16 row stride (16-byte aligned rows)
+    static constexpr int LDS_BYTES = 2 * DV * LDT * 2;
+    static __device__ void stage(unsigned char* smem, const float* S, int tid) {
+        uint16_t* hi = reinterpret_cast<uint16_t*>(smem);
+        uint16_t* lo = hi + DV * LDT;
+        for (int x = tid; x < DK * DV / 4; x += 256) {
+            const int m = x / (DV / 4), j = 4 * (x % (DV / 4));
+            const f32x4 s = *reinterpret_cast<const f32x4*>(S + (size_t)m * DV + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t sh = f32_to_bf16(s[e]);
+                hi[(j + e) * LDT + m] = sh;
+                lo[(j + e) * LDT + m] = f32_to_bf16(s[e] - bf16_to_f32(sh));
+            }
+        }
+    }
+    // Corrections of the 16 tokens whose qt rows start at byte qoff of rq (lane
+    // l % 16 supplies its own token's row), accumulated onto acc[ct].
+    static __device__ void product(const unsigned char* smem, Rsrc rq, uint32_t qoff, f32x4 (&acc)[DV / 16]) {
+        const uint16_t* hi = reinterpret_cast<const uint16_t*>(smem);
+        const uint16_t* lo = hi + DV * LDT;
+        const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            const bf16x8 b = __builtin_bit_cast(bf16x8, buf_ld128(rq, qoff + 2 * (32 * s + 8 * g)));
+#pragma unroll
+            for (int ct = 0; ct < DV / 16; ++ct) {
+                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(hi + (16 * ct + i) * LDT + 32 * s + 8 * g);
+                const bf16x8 al = *reinterpret_cast<const bf16x8*>(lo + (16 * ct + i) * LDT + 32 * s + 8 * g);
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[ct], 0, 0, 0);
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[ct], 0, 0, 0);
+            }
+        }
+    }
+    static __device__ void add_store(Rsrc ro, uint32_t off, f32x4 c) {
+        const u32x2 w = buf_ld64(ro, off);
+        const f32x4 y = {bf16_lo(w[0]) + c[0], bf16_hi(w[0]) + c[1], bf16_lo(w[1]) + c[2], bf16_hi(w[1]) + c[3]};
+        buf_st64(u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])}, ro, off);
+    }
+};
+
+template <int DK, int DV> struct CorrOps<float, DK, DV> {
+    static constexpr int LDT = DK + 4;
+    static constexpr int LDS_BYTES = DV * LDT * 4;
+    static __device__ void stage(unsigned char* smem, const float* S, int tid) {
+        float* st = reinterpret_cast<float*>(smem);
+        for (int x = tid; x < DK * DV / 4; x += 256) {
+            const int m = x / (DV / 4), j = 4 * (x % (DV / 4));
+            const f32x4 s = *reinterpret_cast<const f32x4*>(S + (size_t)m * DV + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(j + e) * LDT + m] = s[e];
+        }
+    }
+    static __device__ void product(const unsigned char* smem, Rsrc rq, uint32_t qoff, f32x4 (&acc)[DV / 16]) {
+        const float* st = reinterpret_cast<const float*>(smem);
+        const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int u = 0; u < DK / 16; ++u) {
+            const u32x4 bw = buf_ld128(rq, qoff + 4 * (16 * u + 4 * g));
+#pragma unroll
+            for (int ct = 0; ct < DV / 16; ++ct) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(st + (16 * ct + i) * LDT + 16 * u + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], __uint_as_float(bw[e]), acc[ct], 0, 0, 0);
+            }
+        }
+    }
+    static __device__ void add_store(Rsrc ro, uint32_t off, f32x4 c) {
+        const u32x4 w = buf_ld128(ro, off);
+        const f32x4 y = {__uint_as_float(w[0]) + c[0], __uint_as_float(w[1]) + c[1], __uint_as_float(w[2]) + c[2],
+                         __uint_as_float(w[3]) + c[3]};
+        buf_st128(__builtin_bit_cast(u32x4, y), ro, off);
+    }
+};
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void split_correct_kernel(const float* __restrict__ ends, const T* __restrict__ qt,
+                                                            T* __restrict__ o, int64_t total_T, int H,
+                                                            int64_t seg_len, int blocks_per_seg, int segments) {
+    using CO = CorrOps<T, DK, DV>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];   // CO::LDS_BYTES
+    int b = blockIdx.x;
+    const int h = b % H;
+    b /= H;
+    const int p = 1 + b / blocks_per_seg;                   // segment
+    const int64_t blk = b % blocks_per_seg;
+    const int64_t seg_end = ((int64_t)p + 1) * seg_len < total_T ? ((int64_t)p + 1) * seg_len : total_T;
+    const int64_t t_begin = (int64_t)p * seg_len + blk * kCorrTok;
+    if (p >= segments || t_begin >= seg_end) return;
+    const int64_t t_end = t_begin + kCorrTok < seg_end ? t_begin + kCorrTok : seg_end;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    CO::stage(smem, ends + ((size_t)(p - 1) * H + h) * DK * DV, tid);
+    __syncthreads();
+
+    // Row ranges: tokens t_begin .. t_end - 1 of this head.  Rows past t_end
+    // read as zero and their stores are dropped.
+    const uint32_t rows = (uint32_t)(t_end - t_begin - 1) * (uint32_t)H + 1u;
+    const Rsrc rq = make_rsrc(qt + ((t_begin - seg_len) * H + h) * DK, rows * DK * (uint32_t)sizeof(T));
+    const Rsrc ro = make_rsrc(o + (t_begin * H + h) * DV, rows * DV * (uint32_t)sizeof(T));
+    for (int64_t t0 = 0; t0 < t_end - t_begin; t0 += 64) {
+        const uint32_t tok = (uint32_t)(t0 + 16 * wave + i);   // this lane's token (operand row)
+        f32x4 acc[DV / 16];
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        CO::product(smem, rq, tok * (uint32_t)H * DK * (uint32_t)sizeof(T), acc);
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct)
+            CO::add_store(ro, (tok * (uint32_t)H * DV + 16 * ct + 4 * g) * (uint32_t)sizeof(T), acc[ct]);
+    }
+}
+
+template <int DK, int DV>
+hipError_t scan_t(const PrefillArgs& a, const SplitWork& w) {
+    const int blocks = a.H * (DV / 16);
+    hipLaunchKernelGGL((split_scan_kernel<DK, DV>), dim3(blocks), dim3(256), 0, a.stream, w.ends, w.phis,
+                       a.final_state, w.segments, a.H);
+    return hipGetLastError();
+}
+
+template <typename T, int DK, int DV>
+hipError_t correct_t(const PrefillArgs& a, const SplitWork& w) {
+    const int64_t bps = (w.seg_len + kCorrTok - 1) / kCorrTok;
+    const int64_t blocks = (int64_t)a.H * (w.segments - 1) * bps;
+    if (blocks <= 0) return hipSuccess;
+    auto kern = split_correct_kernel<T, DK, DV>;
+    constexpr int lds = CorrOps<T, DK, DV>::LDS_BYTES;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), lds, a.stream,
+                       w.ends, (const T*)w.qt, (T*)a.o, a.total_T, a.H, w.seg_len, (int)bps, w.segments);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_split_scan(const PrefillArgs& a, const SplitWork& w) {
+    if (a.d_k == 128) return a.d_v == 128 ? scan_t<128, 128>(a, w) : scan_t<128, 64>(a, w);
+    return a.d_v == 128 ? scan_t<64, 128>(a, w) : scan_t<64, 64>(a, w);
+}
+
+hipError_t launch_split_correct(const PrefillArgs& a, const SplitWork& w) {
+    if (a.bf16) {
+        if (a.d_k == 128) return a.d_v == 128 ? correct_t<uint16_t, 128, 128>(a, w) : correct_t<uint16_t, 128, 64>(a, w);
+        return a.d_v == 128 ? correct_t<uint16_t, 64, 128>(a, w) : correct_t<uint16_t, 64, 64>(a, w);
+    }
+    return a.d_v == 128 ? correct_t<float, 64, 128>(a, w) : correct_t<float, 64, 64>(a, w);
+}
+
+}  // namespace kda

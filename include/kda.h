@@ -23,7 +23,7 @@
  * Ownership: every pointer is caller-owned device memory (any allocation the
  * HIP runtime can address from the current device).  The library neither
  * frees nor retains pointers after a call returns and allocates no device
- * memory of its own.
+ * memory of its own (the time-split prefill takes a caller-owned workspace).
  *
  * Asynchrony: calls validate their arguments on the host, enqueue kernels on
  * `stream` (a hipStream_t; NULL = the legacy default stream) and return; the
@@ -48,6 +48,7 @@
 #ifndef KDA_H_
 #define KDA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -169,6 +170,72 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
                                  float* state, int32_t N, int32_t H,
                                  int32_t d_k, int32_t d_v, kda_dtype dtype,
                                  void* o, void* stream);
+
+/*
+ * kda_chunk_prefill_split -- the prefill of ONE sequence, cut in time into
+ * segments that run at the same time, for shapes whose heads alone would leave
+ * most of the GPU idle (few heads per GPU, e.g. one GPU's share of a head
+ * split across GPUs).
+ *
+ * The section-1.1 recurrence is affine in the state: a run of tokens maps a
+ * start state S to Phi S + B, with Phi the product of the step matrices
+ * (I - beta_t k_t k_t^T) Diag(alpha_t) and B the end state from a zero start.
+ * The call
+ *   1. runs every segment from a zero state (the first from init_state), and
+ *      every segment after the first also from the identity with no values,
+ *      which gives its Phi and Phi_t^T q_t for each of its tokens (Phi_t: the
+ *      product up to token t);
+ *   2. chains the segment end states, S_p = Phi_p S_{p-1} + B_p (fp32);
+ *   3. adds S_{p-1}^T Phi_t^T q_t to the outputs of segment p >= 1.
+ * The result equals kda_chunk_prefill on the same sequence up to rounding
+ * (the correction rounds Phi_t^T q_t to the element type once more).
+ *
+ *   q, k, v, log_alpha, beta, init_state, total_T, H, d_k, d_v, dtype, o,
+ *   final_state : as for kda_chunk_prefill with N = 1 and cu_seqlens NULL.
+ *                 init_state may alias final_state.
+ *   segments    : requested number of segments, >= 1.  Segments are whole
+ *                 64-token chunks; the count actually used is the one that
+ *                 length gives (at most `segments`).  With one segment the call
+ *                 is kda_chunk_prefill (the workspace is not touched and may be
+ *                 NULL).
+ *   workspace   : caller-owned device memory of at least
+ *                 kda_split_workspace_bytes(...) bytes, 16-byte aligned, not
+ *                 overlapping any other argument; its contents on entry do not
+ *                 matter and on return are unspecified.  Calls that share a
+ *                 workspace must be ordered on one stream.
+ *   Returns KDA_ERR_VALUE for segments < 1 or a workspace that is too small,
+ *   KDA_ERR_NULL for a missing workspace when more than one segment is used,
+ *   KDA_ERR_SHAPE when 256 * H * max(d_k, d_v) * (element bytes) exceeds
+ *   2^31 - 1 (the correction's 32-bit offsets).
+ */
+kda_status kda_chunk_prefill_split(const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta, const float* init_state,
+                                   int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                   int32_t segments, void* workspace, size_t workspace_bytes,
+                                   void* o, float* final_state, void* stream);
+
+/* The same from decay / write-strength logits (see the gated calls above). */
+kda_status kda_chunk_prefill_gated_split(const void* q, const void* k, const void* v,
+                                         const void* g_logits, const float* a_log, const float* beta_logits,
+                                         const float* init_state, int64_t total_T, int32_t H,
+                                         int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                         int32_t segments, void* workspace, size_t workspace_bytes,
+                                         void* o, float* final_state, void* stream);
+
+/*
+ * Workspace bytes of a split prefill with these sizes and `segments` requested
+ * (0 when one segment is used or the sizes are invalid).  Host-only; no HIP call.
+ */
+size_t kda_split_workspace_bytes(int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                 int32_t segments);
+
+/*
+ * A segment count for kda_chunk_prefill_split on a GPU with `num_cus` compute
+ * units, from a cost model of the three steps (one prefill workgroup per CU):
+ * 1 when splitting would not pay, e.g. when the heads already fill the GPU.
+ * Host-only; no HIP call.
+ */
+int32_t kda_split_segments(int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, int32_t num_cus);
 
 /*
  * Output epilogue (section 1.3 of the notes, full-rank output gate): the

@@ -209,6 +209,7 @@ def test_empty_calls_are_no_ops():
     assert prefill_epi(lib, T=0, q=None, k=None, v=None, z=None, b=None, og=None, y=None, fin=None) == 0
     assert prologue(lib, T=0, xq=None, xk=None, xv=None, w=None, q=None, k=None, v=None) == 0
     assert decode_fused(lib, N=0, xq=None, w=None, cs=None, S=None, y=None) == 0
+    assert prefill_split(lib, T=0, q=None, k=None, v=None, la=None, b=None, o=None, fin=None, ws=None) == 0
 
 
 def _has_gpu():
@@ -230,8 +231,83 @@ def test_valid_call_without_a_device_reports_no_device():
     assert decode_epi(L.load()) == 5
     assert prologue(L.load()) == 5
     assert decode_fused(L.load()) == 5
+    assert prefill_split(L.load()) == 5
+    assert prefill_split(L.load(), seg=1) == 5
 
 
 def test_binding_raises_when_library_missing(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         L.load(str(tmp_path / "nope.so"))
+
+
+def prefill_split(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, b=P, init=None, T=4096, H=2, dk=64, dv=64, dt=L.KDA_BF16, seg=4, ws=P,
+             wsb=1 << 40, o=P, fin=P)
+    a.update(kw)
+    return lib.kda_chunk_prefill_split(a["q"], a["k"], a["v"], a["la"], a["b"], a["init"], a["T"], a["H"], a["dk"],
+                                       a["dv"], a["dt"], a["seg"], a["ws"], a["wsb"], a["o"], a["fin"], None)
+
+
+def prefill_gated_split(lib, **kw):
+    a = dict(q=P, k=P, v=P, z=P, A=P, b=P, init=None, T=4096, H=2, dk=64, dv=64, dt=L.KDA_BF16, seg=4, ws=P,
+             wsb=1 << 40, o=P, fin=P)
+    a.update(kw)
+    return lib.kda_chunk_prefill_gated_split(a["q"], a["k"], a["v"], a["z"], a["A"], a["b"], a["init"], a["T"],
+                                             a["H"], a["dk"], a["dv"], a["dt"], a["seg"], a["ws"], a["wsb"], a["o"],
+                                             a["fin"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), 3), (dict(seg=0), 7), (dict(seg=-3), 7), (dict(dk=96), 2), (dict(H=0), 2), (dict(T=-1), 2),
+    (dict(H=70000), 2), (dict(dt=L.KDA_F32, dk=128), 2), (dict(ws=None), 1), (dict(q=None), 1), (dict(o=None), 1),
+    (dict(ws=MIS), 4), (dict(la=MIS), 4), (dict(init=MIS), 4), (dict(wsb=1000), 7),
+    (dict(H=40000, dk=128, dv=128), 2), (dict(H=20000, dk=64, dv=128, dt=L.KDA_F32), 2),
+    # one segment is the plain prefill: its own checks apply and no workspace is needed
+    (dict(seg=1, ws=None, q=None), 1), (dict(T=64, seg=8, ws=None, b=None), 1),
+])
+def test_split_prefill_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert prefill_split(L.load(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), 3), (dict(seg=0), 7), (dict(A=None), 1), (dict(z=None), 1), (dict(A=MIS), 4), (dict(ws=None), 1),
+])
+def test_gated_split_prefill_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert prefill_gated_split(L.load(), **kw) == code
+
+
+def test_split_workspace_sizes():
+    """End states, transitions and Phi_t^T q_t rows, each padded to 256 bytes; zero for one segment."""
+    lib = L.load()
+    pad = lambda x: (x + 255) // 256 * 256
+    T, H = 4096, 3          # 64 chunks; 4 segments of 16 chunks (1024 tokens)
+    for dk, dv, dt, es in [(128, 128, L.KDA_BF16, 2), (128, 64, L.KDA_BF16, 2), (64, 128, L.KDA_F32, 4)]:
+        want = pad(4 * H * dk * dv * 4) + pad(3 * H * dk * dk * 4) + pad((T - 1024) * H * dk * es)
+        assert lib.kda_split_workspace_bytes(T, H, dk, dv, dt, 4) == want
+    # 5 requested segments of 64 chunks: 13 chunks each, which gives 5 segments
+    assert lib.kda_split_workspace_bytes(T, 1, 64, 64, L.KDA_BF16, 5) == \
+        pad(5 * 64 * 64 * 4) + pad(4 * 64 * 64 * 4) + pad((T - 13 * 64) * 64 * 2)
+    # 40 requested segments of 3 chunks: one chunk each, which gives 3
+    assert lib.kda_split_workspace_bytes(192, 1, 64, 64, L.KDA_BF16, 40) == \
+        pad(3 * 64 * 64 * 4) + pad(2 * 64 * 64 * 4) + pad(128 * 64 * 2)
+    for T, seg in [(4096, 1), (64, 4), (0, 4)]:
+        assert lib.kda_split_workspace_bytes(T, H, 128, 128, L.KDA_BF16, seg) == 0
+    assert lib.kda_split_workspace_bytes(4096, 0, 128, 128, L.KDA_BF16, 4) == 0
+    assert lib.kda_split_workspace_bytes(4096, H, 96, 128, L.KDA_BF16, 4) == 0
+
+
+def test_split_segment_model():
+    """The cost model keeps one segment when the heads fill the GPU and splits when few heads
+    leave most compute units idle; the count never exceeds the chunk count."""
+    lib = L.load()
+    assert lib.kda_split_segments(65536, 96, 128, 128, 256) == 1
+    assert lib.kda_split_segments(1048576, 96, 128, 128, 256) == 1
+    n12 = lib.kda_split_segments(65536, 12, 128, 128, 256)
+    n1 = lib.kda_split_segments(65536, 1, 128, 128, 256)
+    assert 2 <= n12 < n1
+    assert lib.kda_split_segments(200, 1, 64, 64, 256) <= 4
+    for bad in [(0, 4, 128, 128, 256), (4096, 0, 128, 128, 256), (4096, 4, 96, 128, 256), (4096, 4, 128, 128, 0)]:
+        assert lib.kda_split_segments(*bad) == 1
+    # more compute units never ask for fewer segments
+    counts = [lib.kda_split_segments(65536, 12, 128, 128, c) for c in (64, 128, 256, 512)]
+    assert counts == sorted(counts)
