@@ -300,6 +300,40 @@ def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
                       "~ N(0, 1); same shapes as the headline step"}
 
 
+SPLIT_HEADS = 12    # one GPU's share of the 96 heads under an 8-way head split
+
+
+def time_split(args, dev, stream, ki, lib):
+    """The time-split prefill against the plain one on one GPU's share of a 96-head
+    layer split 8 ways over heads: T = 65,536, H = 12, d = 128, bf16, log-decay
+    U[-5, -3].  The plain kernel fills 24 of the CUs there; the split runs the
+    segments at once (the library's own segment count) and joins them."""
+    import torch
+    T, Hs = T_PREFILL, SPLIT_HEADS
+    x = ki.prefill_inputs([T], H=Hs, d=D, dtype="bf16", la_law="uniform53", init="normal", seed=3, device=dev)
+    o = torch.empty_like(x.v)
+    fin = torch.empty_like(x.init_state)
+    seg = lib.split_segments(T, Hs, D, D, device=dev)
+    ws = torch.empty((max(1, lib.split_workspace_bytes(T, Hs, D, D, torch.bfloat16, seg)),), dtype=torch.uint8,
+                     device=dev)
+    reps = max(1, args.steps)
+    plain_ms = _timed(args, stream, lambda: lib.kda_chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state,
+                                                                  None, o=o, final_state=fin), reps)
+    split_ms = _timed(args, stream, lambda: lib.kda_chunk_prefill_split(x.q, x.k, x.v, x.log_alpha, x.beta,
+                                                                        x.init_state, segments=seg, workspace=ws,
+                                                                        o=o, final_state=fin), reps)
+    byts = T * Hs * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * Hs * STATE_BYTES
+    return {"heads": Hs, "tokens": T, "segments": seg,
+            "plain_ms": round(plain_ms, 4), "plain_tokens_per_s": round(T / (plain_ms * 1e-3), 1),
+            "split_ms": round(split_ms, 4), "split_tokens_per_s": round(T / (split_ms * 1e-3), 1),
+            "speedup": round(plain_ms / split_ms, 3),
+            "split_gbps_algorithmic": round(byts / (split_ms * 1e-3) / 1e9, 1),
+            "split_frac": round(byts / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "config": "kda_chunk_prefill_split vs kda_chunk_prefill, T=65536 H=12 d=128 bf16 (one GPU's share "
+                      "of 96 heads split 8 ways), log-decay U[-5,-3], fp32 state; algorithmic bytes as the "
+                      "plain prefill's"}
+
+
 # Algorithmic bytes (read, written) per launch of each counted kernel, as bench.py runs it.
 _ROWS = T_PREFILL * H
 _PAIRS = N_DECODE * H
@@ -453,6 +487,8 @@ def main():
     ap.add_argument("--no-gated", action="store_true", help="skip the timing of the gated entry points")
     ap.add_argument("--no-epilogue", action="store_true",
                     help="skip the timing of the output epilogue and the input prologue")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the time-split prefill at one GPU's share of the heads (H = 12)")
     ap.add_argument("--capacity", action="store_true",
                     help="also time the 1,048,576-token prefill (about 150 GB of device memory)")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -570,6 +606,10 @@ def main():
         res["epilogue"] = time_epilogue(args, dev, stream, ki, lib)
         torch.cuda.empty_cache()
         res["prologue"] = time_prologue(args, dev, stream, ki, lib)
+    if not args.no_split:
+        torch.cuda.empty_cache()
+        import gated_delta_rule_09_amd as lib
+        res["split"] = time_split(args, dev, stream, ki, lib)
     if args.capacity:
         torch.cuda.empty_cache()
         res["capacity"] = time_capacity(args, dev, stream, ki, kda_chunk_prefill)

@@ -187,11 +187,11 @@ kda_status split_impl(const char* name, const void* q, const void* k, const void
         return prefill_impl(name, q, k, v, decay, beta, a_log, gated, init_state, nullptr, 1, total_T, H, d_k, d_v,
                             dtype, o, final_state, stream);
     if ((int64_t)p.segments * H > (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
-    // The correction addresses 256 tokens of a head with 32-bit byte offsets,
-    // and its grid has one workgroup per (head, 256 tokens of a segment).
+    // The correction addresses 512 tokens of a head with 32-bit byte offsets,
+    // and its grid has one workgroup per (head, 512 tokens of a segment).
     const int64_t es = dtype == KDA_BF16 ? 2 : 4;
-    if (256 * (int64_t)H * (d_k > d_v ? d_k : d_v) * es > (int64_t)INT32_MAX) return KDA_ERR_SHAPE;
-    if ((int64_t)H * (p.segments - 1) * ((p.seg_len + 255) / 256) > (int64_t)INT32_MAX) return KDA_ERR_SHAPE;
+    if (512 * (int64_t)H * (d_k > d_v ? d_k : d_v) * es > (int64_t)UINT32_MAX) return KDA_ERR_SHAPE;
+    if ((int64_t)H * (p.segments - 1) * ((p.seg_len + 511) / 512) > (int64_t)INT32_MAX) return KDA_ERR_SHAPE;
     if (!q || !k || !v || !decay || !beta || !o || (gated && !a_log) || !workspace) return KDA_ERR_NULL;
     const void* ptrs[] = {q, k, v, decay, beta, a_log, init_state, o, final_state, workspace};
     for (const void* ptr : ptrs)

@@ -103,43 +103,57 @@ __global__ __launch_bounds__(256) void split_scan_kernel(float* __restrict__ end
 }
 
 // ---------------------------------------------------------------------------
-// Correction.  One workgroup (4 waves) per (head, segment p >= 1, block of
-// up to 256 tokens of that segment); a wave takes 16 tokens of each 64-token
+// Correction.  One workgroup (8 waves) per (head, segment p >= 1, block of up
+// to 512 tokens of that segment); a wave takes 16 tokens of each 128-token
 // sub-block.  The state that segment p starts from, S = ends[p - 1], is staged
-// transposed in LDS (ST[j][m] = S[m][j]).  The product is formed as
-// D = ST * QT^T, so a lane (n = l % 16, g = l / 16) ends with the correction of
-// token n for the four consecutive value columns 16 ct + 4 g + e.
+// transposed in LDS (ST[j][m] = S[m][j]): a thread takes one column j and 8 (or
+// 4) consecutive rows m, so the global reads are coalesced over j and each
+// LDS write is one 16-byte row piece (conflict-free at that width).  The
+// product is formed as D = ST * QT^T, so a lane (n = l % 16, g = l / 16) ends
+// with the correction of token n for the four consecutive value columns
+// 16 ct + 4 g + e, which is also the layout of its 8- or 16-byte read-modify-
+// write of o.  The o words are loaded beside the qt operands, before the
+// products, so both loads are in flight together.
 // ---------------------------------------------------------------------------
-constexpr int kCorrTok = 256;
+constexpr int kCorrTok = 512;
+constexpr int kCorrThreads = 512;
 
 template <typename T, int DK, int DV> struct CorrOps;
 
 template <int DK, int DV> struct CorrOps<uint16_t, DK, DV> {
     static constexpr int LDT = DK + 8;     // bf16 row stride (16-byte aligned rows)
     static constexpr int LDS_BYTES = 2 * DV * LDT * 2;
+    typedef u32x2 OW;                      // o words of 4 bf16 outputs
     static __device__ void stage(unsigned char* smem, const float* S, int tid) {
         uint16_t* hi = reinterpret_cast<uint16_t*>(smem);
         uint16_t* lo = hi + DV * LDT;
-        for (int x = tid; x < DK * DV / 4; x += 256) {
-            const int m = x / (DV / 4), j = 4 * (x % (DV / 4));
-            const f32x4 s = *reinterpret_cast<const f32x4*>(S + (size_t)m * DV + j);
+        const int j = tid % DV;
+        for (int m0 = 8 * (tid / DV); m0 < DK; m0 += 8 * (kCorrThreads / DV)) {
+            uint32_t wh[4], wl[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint16_t sh = f32_to_bf16(s[e]);
-                hi[(j + e) * LDT + m] = sh;
-                lo[(j + e) * LDT + m] = f32_to_bf16(s[e] - bf16_to_f32(sh));
+            for (int r = 0; r < 8; r += 2) {
+                const float s0 = S[(size_t)(m0 + r) * DV + j], s1 = S[(size_t)(m0 + r + 1) * DV + j];
+                const uint32_t h = pack_bf16x2(s0, s1);
+                wh[r / 2] = h;
+                wl[r / 2] = pack_bf16x2(s0 - bf16_lo(h), s1 - bf16_hi(h));
             }
+            *reinterpret_cast<u32x4*>(hi + j * LDT + m0) = u32x4{wh[0], wh[1], wh[2], wh[3]};
+            *reinterpret_cast<u32x4*>(lo + j * LDT + m0) = u32x4{wl[0], wl[1], wl[2], wl[3]};
         }
     }
-    // Corrections of the 16 tokens whose qt rows start at byte qoff of rq (lane
-    // l % 16 supplies its own token's row), accumulated onto acc[ct].
-    static __device__ void product(const unsigned char* smem, Rsrc rq, uint32_t qoff, f32x4 (&acc)[DV / 16]) {
+    typedef u32x4 QW[DK / 32];            // qt words of one token (B operands)
+    static __device__ void load_q(QW& qw, Rsrc rq, uint32_t qoff) {
+        const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) qw[s] = buf_ld128(rq, qoff + 2 * (32 * s + 8 * g));
+    }
+    static __device__ void product(const unsigned char* smem, const QW& qw, f32x4 (&acc)[DV / 16]) {
         const uint16_t* hi = reinterpret_cast<const uint16_t*>(smem);
         const uint16_t* lo = hi + DV * LDT;
         const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
-            const bf16x8 b = __builtin_bit_cast(bf16x8, buf_ld128(rq, qoff + 2 * (32 * s + 8 * g)));
+            const bf16x8 b = __builtin_bit_cast(bf16x8, qw[s]);
 #pragma unroll
             for (int ct = 0; ct < DV / 16; ++ct) {
                 const bf16x8 ah = *reinterpret_cast<const bf16x8*>(hi + (16 * ct + i) * LDT + 32 * s + 8 * g);
@@ -149,8 +163,8 @@ template <int DK, int DV> struct CorrOps<uint16_t, DK, DV> {
             }
         }
     }
-    static __device__ void add_store(Rsrc ro, uint32_t off, f32x4 c) {
-        const u32x2 w = buf_ld64(ro, off);
+    static __device__ OW load_o(Rsrc ro, uint32_t off) { return buf_ld64(ro, off); }
+    static __device__ void store_o(Rsrc ro, uint32_t off, OW w, f32x4 c) {
         const f32x4 y = {bf16_lo(w[0]) + c[0], bf16_hi(w[0]) + c[1], bf16_lo(w[1]) + c[2], bf16_hi(w[1]) + c[3]};
         buf_st64(u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])}, ro, off);
     }
@@ -159,32 +173,39 @@ template <int DK, int DV> struct CorrOps<uint16_t, DK, DV> {
 template <int DK, int DV> struct CorrOps<float, DK, DV> {
     static constexpr int LDT = DK + 4;
     static constexpr int LDS_BYTES = DV * LDT * 4;
+    typedef u32x4 OW;
     static __device__ void stage(unsigned char* smem, const float* S, int tid) {
         float* st = reinterpret_cast<float*>(smem);
-        for (int x = tid; x < DK * DV / 4; x += 256) {
-            const int m = x / (DV / 4), j = 4 * (x % (DV / 4));
-            const f32x4 s = *reinterpret_cast<const f32x4*>(S + (size_t)m * DV + j);
+        const int j = tid % DV;
+        for (int m0 = 4 * (tid / DV); m0 < DK; m0 += 4 * (kCorrThreads / DV)) {
+            f32x4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) st[(j + e) * LDT + m] = s[e];
+            for (int r = 0; r < 4; ++r) x[r] = S[(size_t)(m0 + r) * DV + j];
+            *reinterpret_cast<f32x4*>(st + j * LDT + m0) = x;
         }
     }
-    static __device__ void product(const unsigned char* smem, Rsrc rq, uint32_t qoff, f32x4 (&acc)[DV / 16]) {
+    typedef u32x4 QW[DK / 16];
+    static __device__ void load_q(QW& qw, Rsrc rq, uint32_t qoff) {
+        const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int u = 0; u < DK / 16; ++u) qw[u] = buf_ld128(rq, qoff + 4 * (16 * u + 4 * g));
+    }
+    static __device__ void product(const unsigned char* smem, const QW& qw, f32x4 (&acc)[DV / 16]) {
         const float* st = reinterpret_cast<const float*>(smem);
         const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
 #pragma unroll
         for (int u = 0; u < DK / 16; ++u) {
-            const u32x4 bw = buf_ld128(rq, qoff + 4 * (16 * u + 4 * g));
 #pragma unroll
             for (int ct = 0; ct < DV / 16; ++ct) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(st + (16 * ct + i) * LDT + 16 * u + 4 * g);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], __uint_as_float(bw[e]), acc[ct], 0, 0, 0);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], __uint_as_float(qw[u][e]), acc[ct], 0, 0, 0);
             }
         }
     }
-    static __device__ void add_store(Rsrc ro, uint32_t off, f32x4 c) {
-        const u32x4 w = buf_ld128(ro, off);
+    static __device__ OW load_o(Rsrc ro, uint32_t off) { return buf_ld128(ro, off); }
+    static __device__ void store_o(Rsrc ro, uint32_t off, OW w, f32x4 c) {
         const f32x4 y = {__uint_as_float(w[0]) + c[0], __uint_as_float(w[1]) + c[1], __uint_as_float(w[2]) + c[2],
                          __uint_as_float(w[3]) + c[3]};
         buf_st128(__builtin_bit_cast(u32x4, y), ro, off);
@@ -192,10 +213,12 @@ template <int DK, int DV> struct CorrOps<float, DK, DV> {
 };
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void split_correct_kernel(const float* __restrict__ ends, const T* __restrict__ qt,
-                                                            T* __restrict__ o, int64_t total_T, int H,
-                                                            int64_t seg_len, int blocks_per_seg, int segments) {
+__global__ __launch_bounds__(kCorrThreads) void split_correct_kernel(const float* __restrict__ ends,
+                                                                     const T* __restrict__ qt, T* __restrict__ o,
+                                                                     int64_t total_T, int H, int64_t seg_len,
+                                                                     int blocks_per_seg, int segments) {
     using CO = CorrOps<T, DK, DV>;
+    static_assert(kCorrThreads % DV == 0, "staging");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];   // CO::LDS_BYTES
     int b = blockIdx.x;
     const int h = b % H;
@@ -217,15 +240,24 @@ __global__ __launch_bounds__(256) void split_correct_kernel(const float* __restr
     const uint32_t rows = (uint32_t)(t_end - t_begin - 1) * (uint32_t)H + 1u;
     const Rsrc rq = make_rsrc(qt + ((t_begin - seg_len) * H + h) * DK, rows * DK * (uint32_t)sizeof(T));
     const Rsrc ro = make_rsrc(o + (t_begin * H + h) * DV, rows * DV * (uint32_t)sizeof(T));
-    for (int64_t t0 = 0; t0 < t_end - t_begin; t0 += 64) {
+    for (int64_t t0 = 0; t0 < t_end - t_begin; t0 += 16 * (kCorrThreads / 64)) {
         const uint32_t tok = (uint32_t)(t0 + 16 * wave + i);   // this lane's token (operand row)
+        const uint32_t orow = tok * (uint32_t)H * DV;
+        typename CO::QW qw;
+        CO::load_q(qw, rq, tok * (uint32_t)H * DK * (uint32_t)sizeof(T));
+        typename CO::OW ow[DV / 16];
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct) ow[ct] = CO::load_o(ro, (orow + 16 * ct + 4 * g) * (uint32_t)sizeof(T));
+        // The staged operands are read again for every sub-block rather than
+        // held in registers, which keeps room for more waves per SIMD.
+        __asm__ volatile("" ::: "memory");
         f32x4 acc[DV / 16];
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        CO::product(smem, rq, tok * (uint32_t)H * DK * (uint32_t)sizeof(T), acc);
+        CO::product(smem, qw, acc);
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct)
-            CO::add_store(ro, (tok * (uint32_t)H * DV + 16 * ct + 4 * g) * (uint32_t)sizeof(T), acc[ct]);
+            CO::store_o(ro, (orow + 16 * ct + 4 * g) * (uint32_t)sizeof(T), ow[ct], acc[ct]);
     }
 }
 
@@ -246,7 +278,7 @@ hipError_t correct_t(const PrefillArgs& a, const SplitWork& w) {
     constexpr int lds = CorrOps<T, DK, DV>::LDS_BYTES;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), lds, a.stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kCorrThreads), lds, a.stream,
                        w.ends, (const T*)w.qt, (T*)a.o, a.total_T, a.H, w.seg_len, (int)bps, w.segments);
     return hipGetLastError();
 }

@@ -205,8 +205,8 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
  *                 workspace must be ordered on one stream.
  *   Returns KDA_ERR_VALUE for segments < 1 or a workspace that is too small,
  *   KDA_ERR_NULL for a missing workspace when more than one segment is used,
- *   KDA_ERR_SHAPE when 256 * H * max(d_k, d_v) * (element bytes) exceeds
- *   2^31 - 1 (the correction's 32-bit offsets).
+ *   KDA_ERR_SHAPE when 512 * H * max(d_k, d_v) * (element bytes) exceeds
+ *   2^32 - 1 (the correction's 32-bit offsets).
  */
 kda_status kda_chunk_prefill_split(const void* q, const void* k, const void* v,
                                    const float* log_alpha, const float* beta, const float* init_state,
