@@ -99,6 +99,8 @@ KERNEL_SOURCES = {
                  "gated_delta_rule_09_amd/csrc/kda_internal.h"],
     "prologue": ["gated_delta_rule_09_amd/csrc/kda_prologue.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
                  "gated_delta_rule_09_amd/csrc/kda_internal.h"],
+    "split": ["gated_delta_rule_09_amd/csrc/kda_split.hip", "gated_delta_rule_09_amd/csrc/kda_device.h",
+              "gated_delta_rule_09_amd/csrc/kda_internal.h"],
 }
 
 
@@ -381,11 +383,14 @@ def _read_dispatches(path):
 
 
 def _label_dispatches(disp):
-    """Name each dispatch of a `bench.py --no-gated` run after the kernel and the step it belongs to:
-    a prologue followed by a gated prefill is part of the timed layer (not labelled), and an epilogue
-    directly after a gated prefill is the gated prefill's epilogue."""
+    """Name each dispatch of a `bench.py --no-gated --no-split` run after the kernel and the step it
+    belongs to: a prologue followed by a gated prefill is part of the timed layer (not labelled), and
+    an epilogue directly after a gated prefill is the gated prefill's epilogue.  A run with the split
+    timing is refused: its 12-head prefills launch the same kernel as the headline prefill."""
     import re
     names = [d[0] for d in disp]
+    if any("split_scan_kernel" in n or "split_correct_kernel" in n for n in names):
+        raise SystemExit("the counter runs must be made with --no-split")
     labels = []
     for i, n in enumerate(names):
         m = re.search(r"prefill_kernel<[^,]+, 128, 128, (true|false)>", n)
@@ -412,7 +417,7 @@ def _label_dispatches(disp):
 
 def record_counters(pmc_dir: str, copy_gib: float):
     """Build profiles/hbm_traffic.json from three rocprofv3 runs of
-    `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-gated --calibrate-copy-gib G` stored under
+    `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-gated --no-split --calibrate-copy-gib G` stored under
     pmc_dir/fetch (--pmc FETCH_SIZE), pmc_dir/write (--pmc WRITE_SIZE) and pmc_dir/util
     (--pmc MfmaUtil VALUBusy), each a results DB or --output-format csv.  HBM bytes are the counters scaled by what they read for the plain
     copy of G GiB; every record carries the code digest of its kernel's sources."""

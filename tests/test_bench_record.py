@@ -30,6 +30,15 @@ def test_labels_follow_kernel_and_position():
                       "prefill_gated", "epilogue_after_prefill", "decode_fused"]
 
 
+def test_labels_refuse_a_run_with_the_split_timing():
+    """The 12-head prefills of the split timing launch the headline prefill's kernel, so their
+    counters would be averaged into it: such a run is refused."""
+    import pytest
+    scan = "void kda::(anonymous namespace)::split_scan_kernel<128, 128>(float*, float const*, float*, int, int)"
+    with pytest.raises(SystemExit, match="--no-split"):
+        bench._label_dispatches([(n, {}) for n in _sequence() + [PRE.format("false"), scan]])
+
+
 def test_algorithmic_bytes_match_the_per_launch_figures():
     r, w = bench.ALG_BYTES["prefill"]
     assert r + w == bench.T_PREFILL * bench.H * bench.PREFILL_BYTES_PER_TOKEN_HEAD + 2 * bench.H * bench.STATE_BYTES
