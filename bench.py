@@ -305,6 +305,28 @@ def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
 SPLIT_HEADS = 12    # one GPU's share of the 96 heads under an 8-way head split
 
 
+def time_split_capacity(args, dev, stream, ki, lib):
+    """The time split at the capacity length: one sequence of T = 1,048,576 tokens at
+    H = 12 (one GPU's share of 96 heads split 8 ways), d = 128, bf16, log-decay U[-5, -3]."""
+    import torch
+    T, Hs = 1 << 20, SPLIT_HEADS
+    x = ki.prefill_inputs([T], H=Hs, d=D, dtype="bf16", la_law="uniform53", init="normal", seed=3, device=dev)
+    o = torch.empty_like(x.v)
+    fin = torch.empty_like(x.init_state)
+    seg = lib.split_segments(T, Hs, D, D, device=dev)
+    ws = torch.empty((max(1, lib.split_workspace_bytes(T, Hs, D, D, torch.bfloat16, seg)),), dtype=torch.uint8,
+                     device=dev)
+    reps = max(1, min(args.steps, 3))
+    plain_ms = _timed(args, stream, lambda: lib.kda_chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state,
+                                                                  None, o=o, final_state=fin), reps)
+    split_ms = _timed(args, stream, lambda: lib.kda_chunk_prefill_split(x.q, x.k, x.v, x.log_alpha, x.beta,
+                                                                        x.init_state, segments=seg, workspace=ws,
+                                                                        o=o, final_state=fin), reps)
+    return {"heads": Hs, "tokens": T, "segments": seg, "plain_ms": round(plain_ms, 3),
+            "split_ms": round(split_ms, 3), "split_tokens_per_s": round(T / (split_ms * 1e-3), 1),
+            "speedup": round(plain_ms / split_ms, 3)}
+
+
 def time_split(args, dev, stream, ki, lib):
     """The time-split prefill against the plain one on one GPU's share of a 96-head
     layer split 8 ways over heads: T = 65,536, H = 12, d = 128, bf16, log-decay
@@ -495,7 +517,8 @@ def main():
     ap.add_argument("--no-split", action="store_true",
                     help="skip the time-split prefill at one GPU's share of the heads (H = 12)")
     ap.add_argument("--capacity", action="store_true",
-                    help="also time the 1,048,576-token prefill (about 150 GB of device memory)")
+                    help="also time the 1,048,576-token prefill (about 150 GB of device memory), and the time "
+                         "split at that length with 12 heads")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (counter calibration)")
     ap.add_argument("--record-counters", metavar="PMC_DIR",
@@ -618,6 +641,10 @@ def main():
     if args.capacity:
         torch.cuda.empty_cache()
         res["capacity"] = time_capacity(args, dev, stream, ki, kda_chunk_prefill)
+        if not args.no_split:
+            torch.cuda.empty_cache()
+            import gated_delta_rule_09_amd as lib
+            res["capacity_split"] = time_split_capacity(args, dev, stream, ki, lib)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)
