@@ -55,20 +55,36 @@ FUSED_DECODE_BYTES_PER_PAIR = EPILOGUE_DECODE_BYTES_PER_PAIR + 2 * 3 * CONV_C * 
 PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 2 * 64 * (D + D)              # 131,072
 
 
-def cpu_baseline(budget_s: float = 12.0):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(budget_s: float = 12.0, max_workers: int = 16):
     """Time the fp64 oracle (as it stands) on a bounded sample of the prefill
-    workload: 8 heads of the 64K-token sequence, consecutive 1024-token
-    segments with the state carried, until the time budget is spent.  Runs in
-    a single-threaded subprocess so that `cores` is exact."""
+    workload.  Up to `max_workers` single-threaded processes (one per available
+    core) each run 8 heads of the 64K-token sequence, consecutive 1024-token
+    segments with the state carried, until the time budget is spent; the heads
+    are independent, so the processes share nothing.  `cores` is the number of
+    processes."""
     code = r"""
 import json, sys, time
 sys.path.insert(0, %r)
 import numpy as np
 import kda_inputs as ki
 import oracle
-x = ki.prefill_inputs([65536], H=8, d=%d, dtype="bf16", la_law="uniform53", init="normal", seed=3)
+w = int(sys.argv[1])
+x = ki.prefill_inputs([65536], H=8, d=%d, dtype="bf16", la_law="uniform53", init="normal", seed=3 + w)
 n = ki.to_numpy
 q, k, v, la, b, S = (n(x.q), n(x.k), n(x.v), n(x.log_alpha), n(x.beta), n(x.init_state)[0].astype(np.float64))
+print("ready", flush=True)
+sys.stdin.readline()
 done, t0 = 0, time.perf_counter()
 while done < q.shape[0]:
     sl = slice(done, done + 1024)
@@ -77,17 +93,34 @@ while done < q.shape[0]:
     if time.perf_counter() - t0 > %f:
         break
 dt = time.perf_counter() - t0
-print(json.dumps({"token_heads": done * 8, "seconds": dt}))
+print(json.dumps({"token_heads": done * 8, "seconds": dt}), flush=True)
 """ % (ROOT, D, budget_s)
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
-    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
-    if out.returncode != 0:
-        raise RuntimeError(out.stderr[-2000:])
-    r = json.loads(out.stdout.strip().splitlines()[-1])
-    th_per_s = r["token_heads"] / r["seconds"]
-    return {"value": th_per_s / H, "unit": "tokens/s (H=96 equivalent)", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 oracle, 8 heads x {r['token_heads'] // 8} tokens of the 64K prefill workload "
-                      f"({r['seconds']:.1f} s, {th_per_s:.0f} token-heads/s, single thread)"}
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    procs = [subprocess.Popen([sys.executable, "-c", code, str(w)], stdin=subprocess.PIPE, stdout=subprocess.PIPE,
+                              stderr=subprocess.PIPE, text=True, env=env) for w in range(workers)]
+    try:
+        # Every process draws its inputs first; the timed loops then start together.
+        for p in procs:
+            if p.stdout.readline().strip() != "ready":
+                raise RuntimeError(p.stderr.read()[-2000:])
+        t0 = time.perf_counter()
+        for p in procs:
+            p.stdin.write("go\n")
+            p.stdin.flush()
+        res = [json.loads(p.communicate(timeout=600)[0].strip().splitlines()[-1]) for p in procs]
+        wall = time.perf_counter() - t0
+    finally:
+        for p in procs:
+            if p.poll() is None:
+                p.kill()
+    token_heads = sum(r["token_heads"] for r in res)
+    th_per_s = token_heads / wall
+    return {"value": th_per_s / H, "unit": "tokens/s (H=96 equivalent)", "cores": workers, "kind": "oracle",
+            "sample": f"fp64 oracle, {workers} single-threaded process{'es' if workers > 1 else ''} x 8 heads x "
+                      f"{min(r['token_heads'] for r in res) // 8}-{max(r['token_heads'] for r in res) // 8} tokens "
+                      f"of the 64K prefill workload ({wall:.1f} s wall, {th_per_s:.0f} token-heads/s) on "
+                      f"{_cpu_model()}"}
 
 
 KERNEL_SOURCES = {
