@@ -311,3 +311,21 @@ def test_split_segment_model():
     # more compute units never ask for fewer segments
     counts = [lib.kda_split_segments(65536, 12, 128, 128, c) for c in (64, 128, 256, 512)]
     assert counts == sorted(counts)
+
+
+def test_split_binding_checks_before_calling_the_library():
+    """The split wrapper rejects a wrong initial-state shape or a wrong decay dtype itself, and
+    sizes the workspace with the library's own function."""
+    import torch
+    T, H, d = 256, 2, 64
+    q = torch.zeros(T, H, d, dtype=torch.bfloat16)
+    la = torch.zeros(T, H, d)
+    b = torch.zeros(T, H)
+    with pytest.raises(ValueError, match="init_state"):
+        L.kda_chunk_prefill_split(q, q, q, la, b, init_state=torch.zeros(2, H, d, d), segments=2)
+    with pytest.raises(TypeError, match="decay"):
+        L.kda_chunk_prefill_split(q, q, q, la.double(), b, segments=2)
+    lib = L.load()
+    assert L.split_workspace_bytes(T, H, d, d, torch.bfloat16, 2) == \
+        lib.kda_split_workspace_bytes(T, H, d, d, L.KDA_BF16, 2) > 0
+    assert L.split_workspace_bytes(T, H, d, d, torch.float32, 1) == 0
