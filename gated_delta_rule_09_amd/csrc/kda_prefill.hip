@@ -51,6 +51,11 @@
 // value-column workgroups of a head are placed 8 workgroups apart so that they
 // land on the same XCD and share its L2.
 //
+// A launch runs one or two jobs (PrefillJob) over the same q, k, decay and
+// beta: the plain entry point runs one; the time split of one sequence runs
+// its zero-state segment runs and its identity-state transition runs as two
+// jobs of one launch (kda_split.hip has the other two steps).
+//
 // One MFMA shape per accumulator chain: on gfx950, a 16x16x16 bf16 MFMA that
 // accumulates directly onto the result of a 16x16x32 bf16 MFMA was seen to
 // read stale accumulator registers.  Every chain that mixes K = 16 and K = 32
