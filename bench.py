@@ -7,15 +7,21 @@ and beta, fp32 state) followed by one decode step of the batched-decode
 workload (512 sequences x 96 heads, fp32 state of 3.2 GB updated in place).
 Inputs are synthetic, seeded, and resident in device memory before timing.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--capacity]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gated]
+                    [--no-epilogue] [--no-split] [--capacity]
 
 Prints one JSON line.  `value` is prefill tokens/s; decode state-update
-bandwidth is reported under "decode"; the gated entry points, the output
-epilogue (standalone, after the gated prefill, fused into the gated decode)
-and the input prologue (standalone, the whole prefill layer core, the
-one-kernel decode step) are timed after the headline step under "gated",
-"epilogue" and "prologue".  Kernel durations come from HIP events
-recorded on the stream the kernels are launched on.
+bandwidth is reported under "decode".  Timed after the headline step:
+- "gated": the gated entry points;
+- "epilogue": the output epilogue (standalone, after the gated prefill, fused
+  into the gated decode);
+- "prologue": the input prologue (standalone, the whole prefill layer core,
+  the one-kernel decode step);
+- "split": the time-split prefill against the plain one at one GPU's share of
+  the heads (H = 12).
+Kernel durations come from HIP events recorded on the stream the kernels are
+launched on.  `python bench.py --record-counters DIR` builds the HBM traffic
+record from rocprofv3 counter runs instead (no GPU).
 """
 
 import argparse
