@@ -18,7 +18,8 @@ bandwidth is reported under "decode".  Timed after the headline step:
 - "prologue": the input prologue (standalone, the whole prefill layer core,
   the one-kernel decode step);
 - "split": the time-split prefill against the plain one at one GPU's share of
-  the heads (H = 12).
+  the heads (H = 12);
+- "varlen": the packed workload of 16 sequences of 1K to 8K tokens.
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on.  `python bench.py --record-counters DIR` builds the HBM traffic
 record from rocprofv3 counter runs instead (no GPU).
@@ -339,6 +340,23 @@ def time_gated(args, dev, stream, ki, prefill_gated, decode_gated):
             "decode_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "config": "gated entry points: bf16 decay logits z ~ N(0, 4), A_h ~ U[-1, 1], fp32 beta logits "
                       "~ N(0, 1); same shapes as the headline step"}
+
+
+def time_varlen(args, dev, stream, ki, prefill):
+    """The packed workload: 16 sequences of U{1024..8192} tokens, H = 96, d = 128,
+    bf16, each with its own initial and final state (3,072 workgroups, enough to
+    occupy every CU, unlike the single 64K sequence)."""
+    import torch
+    x = ki.workload_inputs("varlen16", device=dev)
+    T = x.q.shape[0]
+    N = x.cu_seqlens.shape[0] - 1
+    o = torch.empty_like(x.v)
+    fin = torch.empty_like(x.init_state)
+    ms = _timed(args, stream, lambda: prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state, x.cu_seqlens,
+                                              o=o, final_state=fin), max(1, args.steps))
+    byts = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * N * H * STATE_BYTES
+    return {"sequences": N, "tokens": T, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "gbps": round(byts / (ms * 1e-3) / 1e9, 1), "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 SPLIT_HEADS = 12    # one GPU's share of the 96 heads under an 8-way head split
@@ -664,6 +682,7 @@ def main():
                                 "traffic": measured_traffic("decode", dec_ms),
                                 "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec_bytes}},
     }
+    res["varlen"] = time_varlen(args, dev, stream, ki, kda_chunk_prefill)
     if not args.no_gated:
         res["gated"] = time_gated(args, dev, stream, ki, kda_chunk_prefill_gated, kda_decode_step_gated)
     if not args.no_epilogue:
