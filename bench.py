@@ -8,7 +8,7 @@ workload (512 sequences x 96 heads, fp32 state of 3.2 GB updated in place).
 Inputs are synthetic, seeded, and resident in device memory before timing.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gated]
-                    [--no-epilogue] [--no-split] [--capacity]
+                    [--no-epilogue] [--no-split] [--no-varlen] [--capacity]
 
 Prints one JSON line.  `value` is prefill tokens/s; decode state-update
 bandwidth is reported under "decode".  Timed after the headline step:
@@ -440,12 +440,16 @@ def _read_dispatches(path):
     results DB or its counter_collection.csv."""
     if path.endswith(".csv"):
         import csv
-        acc = {}
+        acc, grids = {}, {}
         with open(path, newline="") as fh:
             for r in csv.DictReader(fh):
                 key = (int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"])
                 acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+                if r.get("Grid_Size"):
+                    grids[int(r["Dispatch_Id"])] = float(r["Grid_Size"])
         rows = sorted((d, n, c, v) for (d, n, c), v in acc.items())
+        rows += [(d, None, "_grid", g) for d, g in grids.items()]
+        rows.sort(key=lambda t: t[0])
     else:
         import sqlite3
         con = sqlite3.connect(path)
@@ -457,12 +461,14 @@ def _read_dispatches(path):
         if disp not in idx:
             idx[disp] = len(out)
             out.append((name, {}))
+        if name is not None and out[idx[disp]][0] is None:
+            out[idx[disp]] = (name, out[idx[disp]][1])
         out[idx[disp]][1][counter] = value
     return out
 
 
 def _label_dispatches(disp):
-    """Name each dispatch of a `bench.py --no-gated --no-split` run after the kernel and the step it
+    """Name each dispatch of a `bench.py --no-gated --no-split --no-varlen` run after the kernel and the step it
     belongs to: a prologue followed by a gated prefill is part of the timed layer (not labelled), and
     an epilogue directly after a gated prefill is the gated prefill's epilogue.  A run with the split
     timing is refused: its 12-head prefills launch the same kernel as the headline prefill."""
@@ -491,12 +497,22 @@ def _label_dispatches(disp):
             labels.append(None if next_gp else "prologue")
         else:
             labels.append(None)
+    # Every dispatch of one label must have one launch shape (the varlen timing launches the
+    # headline prefill's kernel on another grid).
+    grids = {}
+    for lab, (_, c) in zip(labels, disp):
+        if lab is not None and "_grid" in c:
+            grids.setdefault(lab, set()).add(c["_grid"])
+    if any(len(g) > 1 for g in grids.values()):
+        raise SystemExit("dispatches of one kernel on different grids: make the counter runs with "
+                         "--no-gated --no-split --no-varlen")
     return labels
 
 
 def record_counters(pmc_dir: str, copy_gib: float):
     """Build profiles/hbm_traffic.json from three rocprofv3 runs of
-    `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-gated --no-split --calibrate-copy-gib G` stored under
+    `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-gated --no-split --no-varlen --calibrate-copy-gib G`
+    stored under
     pmc_dir/fetch (--pmc FETCH_SIZE), pmc_dir/write (--pmc WRITE_SIZE) and pmc_dir/util
     (--pmc MfmaUtil VALUBusy), each a results DB or --output-format csv.  HBM bytes are the counters scaled by what they read for the plain
     copy of G GiB; every record carries the code digest of its kernel's sources."""
@@ -571,6 +587,7 @@ def main():
     ap.add_argument("--no-gated", action="store_true", help="skip the timing of the gated entry points")
     ap.add_argument("--no-epilogue", action="store_true",
                     help="skip the timing of the output epilogue and the input prologue")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the timing of the packed varlen workload")
     ap.add_argument("--no-split", action="store_true",
                     help="skip the time-split prefill at one GPU's share of the heads (H = 12)")
     ap.add_argument("--capacity", action="store_true",
@@ -682,7 +699,8 @@ def main():
                                 "traffic": measured_traffic("decode", dec_ms),
                                 "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec_bytes}},
     }
-    res["varlen"] = time_varlen(args, dev, stream, ki, kda_chunk_prefill)
+    if not args.no_varlen:
+        res["varlen"] = time_varlen(args, dev, stream, ki, kda_chunk_prefill)
     if not args.no_gated:
         res["gated"] = time_gated(args, dev, stream, ki, kda_chunk_prefill_gated, kda_decode_step_gated)
     if not args.no_epilogue:

@@ -39,6 +39,18 @@ def test_labels_refuse_a_run_with_the_split_timing():
         bench._label_dispatches([(n, {}) for n in _sequence() + [PRE.format("false"), scan]])
 
 
+def test_labels_refuse_one_kernel_on_two_grids():
+    """The varlen timing launches the headline prefill's kernel on another grid; a run that
+    includes it is refused, while one grid per label is accepted."""
+    import pytest
+    seq = _sequence()
+    same = [(n, {"_grid": 98304.0} if "prefill_kernel" in n else {}) for n in seq]
+    bench._label_dispatches(same)
+    mixed = same + [(PRE.format("false"), {"_grid": 1572864.0})]
+    with pytest.raises(SystemExit, match="--no-varlen"):
+        bench._label_dispatches(mixed)
+
+
 def test_algorithmic_bytes_match_the_per_launch_figures():
     r, w = bench.ALG_BYTES["prefill"]
     assert r + w == bench.T_PREFILL * bench.H * bench.PREFILL_BYTES_PER_TOKEN_HEAD + 2 * bench.H * bench.STATE_BYTES
