@@ -137,3 +137,33 @@ def test_split_at_full_length_twelve_heads_sampled():
     o_ref, f_ref = oracle.kda_prefill(host(x.q), host(x.k), host(x.v), host(x.log_alpha), host(x.beta),
                                       host(x.init_state), heads=heads)
     _check(o, fin, o_ref, f_ref, "bf16", f"heads {heads}", heads=heads)
+
+
+@pytest.mark.parametrize("gated,d_v", [(True, 128), (False, 64)])
+def test_split_at_full_length_gated_and_mixed_widths(gated, d_v):
+    """T = 65,536, H = 12 with the library's segment count: the gated split, and d_v = 64 < d_k
+    (the segment runs and the transition runs are then two launches).  Against the unsplit
+    kernel on every head and the fp64 oracle on one sampled head."""
+    T, H, d = 65536, 12, 128
+    seg = split_segments(T, H, d, d_v)
+    announce(f"split prefill T={T} H={H} d_k={d} d_v={d_v} gated={gated}: {seg} segments")
+    h = [int(np.random.default_rng(28).integers(H))]
+    if gated:
+        x = ki.gated_inputs([T], H, d, dtype="bf16", init="normal", seed=28, device=device(), d_v=d_v)
+        o, fin = kda_chunk_prefill_gated_split(x.q, x.k, x.v, x.g_logits, x.a_log, x.beta_logits, x.init_state,
+                                               segments=seg)
+        o_plain, f_plain = kda_chunk_prefill_gated(x.q, x.k, x.v, x.g_logits, x.a_log, x.beta_logits, x.init_state)
+        torch.cuda.synchronize()
+        o_ref, f_ref = oracle.kda_prefill_gated(host(x.q), host(x.k), host(x.v), host(x.g_logits), host(x.a_log),
+                                                host(x.beta_logits), host(x.init_state), heads=h)
+    else:
+        x = ki.prefill_inputs([T], H=H, d=d, d_v=d_v, dtype="bf16", init="normal", seed=28, device=device())
+        o, fin = kda_chunk_prefill_split(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state, segments=seg)
+        o_plain, f_plain = kda_chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state)
+        torch.cuda.synchronize()
+        o_ref, f_ref = oracle.kda_prefill(host(x.q), host(x.k), host(x.v), host(x.log_alpha), host(x.beta),
+                                          host(x.init_state), heads=h)
+    assert seg > 1
+    assert rel_err(host(o), host(o_plain)) <= TOL["bf16"]
+    assert rel_err(host(fin), host(f_plain)) <= TOL["bf16"]
+    _check(o, fin, o_ref, f_ref, "bf16", f"head {h}", heads=h)
