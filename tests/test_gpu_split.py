@@ -10,7 +10,8 @@ import kda_inputs as ki
 import oracle
 from gpu_util import TOL, announce, device, host, rel_err
 from gated_delta_rule_09_amd import (kda_chunk_prefill, kda_chunk_prefill_gated, kda_chunk_prefill_gated_split,
-                                     kda_chunk_prefill_split, split_segments, split_workspace_bytes)
+                                     kda_chunk_prefill_split, kda_decode_step, split_segments,
+                                     split_workspace_bytes)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,3 +168,25 @@ def test_split_at_full_length_gated_and_mixed_widths(gated, d_v):
     assert rel_err(host(o), host(o_plain)) <= TOL["bf16"]
     assert rel_err(host(fin), host(f_plain)) <= TOL["bf16"]
     _check(o, fin, o_ref, f_ref, "bf16", f"head {h}", heads=h)
+
+
+def test_split_state_continues_into_decode():
+    """A split prefill of T - 5 tokens followed by 5 decode steps from its final state gives the
+    last 5 outputs and the final state of the whole run (fp64 oracle over all T tokens)."""
+    T, H = 2053, 2
+    x = ki.prefill_inputs([T], H=H, d=128, dtype="bf16", init="normal", seed=29, device=device())
+    announce(f"split prefill of {T - 5} tokens (4 segments) + 5 decode steps vs the oracle over {T}")
+    t = T - 5
+    _, state = kda_chunk_prefill_split(x.q[:t].clone(), x.k[:t].clone(), x.v[:t].clone(), x.log_alpha[:t].clone(),
+                                       x.beta[:t].clone(), x.init_state, segments=4)
+    outs = []
+    for s_ in range(t, T):
+        sl = lambda a: a[s_:s_ + 1].clone()
+        outs.append(kda_decode_step(sl(x.q), sl(x.k), sl(x.v), sl(x.log_alpha), sl(x.beta), state))
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle.kda_prefill(host(x.q), host(x.k), host(x.v), host(x.log_alpha), host(x.beta),
+                                      host(x.init_state))
+    eo = rel_err(host(torch.cat(outs)), o_ref[t:])
+    es = rel_err(host(state), f_ref)
+    announce(f"  tail o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
