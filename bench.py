@@ -649,8 +649,11 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    pre_all = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    dec_all = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    pre_ms = sum(pre_all) / args.steps
+    dec_ms = sum(dec_all) / args.steps
+    median = lambda v: (v[(len(v) - 1) // 2] + v[len(v) // 2]) / 2
 
     if args.calibrate_copy_gib > 0:
         nbytes = int(args.calibrate_copy_gib * (1 << 30))
@@ -689,11 +692,13 @@ def main():
                      "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic("prefill", pre_ms),
                      "kernel": "prefill_kernel", "avg_launch_ms": round(pre_ms, 4),
+                     "median_launch_ms": round(median(pre_all), 4),
                      "algorithmic_bytes_per_launch": pre_bytes,
                      "mfma_frac_algorithmic": round(pre_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
                      "mfma_util_rocprof_pct": measured_util("prefill")[0],
                      "valu_busy_rocprof_pct": measured_util("prefill")[1]},
         "decode": {"gbps": round(dec_gbps, 1), "ms_per_step": round(dec_ms, 4),
+                   "median_ms_per_step": round(median(dec_all), 4),
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                                 "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                                 "traffic": measured_traffic("decode", dec_ms),
