@@ -443,8 +443,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     static_assert((LPR == 8 || LPR == 16) && RP >= 2, "SI mapping");
     static_assert(NV == 1 || NV == 2, "value blocking");
 
-    // Workgroup -> (unit = sequence * H + head, value block).  With two value
-    // blocks, the pair of a unit sits 8 workgroups apart (same XCD).
+    // Workgroup -> (unit = sequence * H + head, value block); in the jobs of a
+    // time split a "sequence" is one segment.  With two value blocks, the pair
+    // of a unit sits 8 workgroups apart (same XCD).
     const int lid = (int)blockIdx.x - (second ? j0.blocks : 0);
     int unit, vblk;
     if constexpr (NV == 2) {
