@@ -8,7 +8,7 @@ workload (512 sequences x 96 heads, fp32 state of 3.2 GB updated in place).
 Inputs are synthetic, seeded, and resident in device memory before timing.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gated]
-                    [--no-epilogue] [--no-split] [--no-varlen] [--capacity]
+                    [--no-epilogue] [--no-split] [--no-varlen] [--capacity] [--cpu-baselines]
 
 Prints one JSON line.  `value` is prefill tokens/s; decode state-update
 bandwidth is reported under "decode".  Timed after the headline step:
@@ -21,7 +21,9 @@ bandwidth is reported under "decode".  Timed after the headline step:
   the heads (H = 12);
 - "varlen": the packed workload of 16 sequences of 1K to 8K tokens.
 Kernel durations come from HIP events recorded on the stream the kernels are
-launched on.  `python bench.py --record-counters DIR` builds the HBM traffic
+launched on.  "wait_giveups" counts bounded in-kernel waits that ran out
+(0 when every wait ended normally).  --cpu-baselines adds the fp64 oracle
+timed beside every workload on the host cores.  `python bench.py --record-counters DIR` builds the HBM traffic
 record from rocprofv3 counter runs instead (no GPU).
 """
 
@@ -128,6 +130,87 @@ print(json.dumps({"token_heads": done * 8, "seconds": dt}), flush=True)
                       f"{min(r['token_heads'] for r in res) // 8}-{max(r['token_heads'] for r in res) // 8} tokens "
                       f"of the 64K prefill workload ({wall:.1f} s wall, {th_per_s:.0f} token-heads/s) on "
                       f"{_cpu_model()}"}
+
+
+DECODE_WORKER = r"""
+import json, sys, time
+sys.path.insert(0, %r)
+import numpy as np
+import kda_inputs as ki
+import oracle
+w, n_seq, steps = int(sys.argv[1]), int(sys.argv[2]), int(sys.argv[3])
+S = ki.decode_state(n_seq, 96, 128, seed=4 + 1000 * w).numpy().astype(np.float64)
+xs = [{k: ki.to_numpy(v) for k, v in ki.decode_inputs(n_seq, 96, 128, seed=4 + 1000 * w, step=t).items()}
+      for t in range(steps)]
+print("ready", flush=True)
+sys.stdin.readline()
+t0 = time.perf_counter()
+for x in xs:
+    _, S = oracle.kda_decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], S)
+print(json.dumps({"seconds": time.perf_counter() - t0, "pair_steps": n_seq * 96 * steps}), flush=True)
+"""
+
+
+def cpu_baselines():
+    """The fp64 oracle timed beside every workload on the host cores (inputs of
+    the same laws and shapes drawn on the host): the tiny workload in full, the
+    4K workload on all 96 heads, the packed varlen workload in full, the long
+    workloads on 4 heads (64K and 1M tokens), and the decode workload's 100
+    steps on all 512 x 96 pairs.  Prefill heads run in child processes, one
+    slice of heads each; the decode pairs in 16 processes of 32 sequences."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import numpy as np
+    import kda_inputs as ki
+    import oracle
+    import oracle_pool
+    cores = oracle_pool.host_cores()
+    out = {"cpu": oracle_pool.cpu_model(), "cores": cores, "kind": "oracle", "unit": "seconds of wall time"}
+
+    def pool_run(name, x, heads=None, workers=None):
+        r = oracle_pool.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state, x.cu_seqlens, heads=heads,
+                                workers=workers)
+        out[name] = {"seconds": round(r["seconds"], 3), "token_heads": r["token_heads"], "processes": r["workers"],
+                     "token_heads_per_s": round(r["token_heads"] / r["seconds"], 1)}
+        print(f"[cpu-baselines] {name}: {out[name]}", file=sys.stderr, flush=True)
+
+    x = ki.workload_inputs("tiny_fp32")
+    n = ki.to_numpy
+    t0 = time.perf_counter()
+    oracle.kda_prefill(n(x.q), n(x.k), n(x.v), n(x.log_alpha), n(x.beta), None)
+    dt = time.perf_counter() - t0
+    out["tiny_fp32"] = {"seconds": round(dt, 3), "token_heads": 512, "processes": 1,
+                        "token_heads_per_s": round(512 / dt, 1)}
+    pool_run("bf16_4k_96_heads", ki.workload_inputs("bf16_4k"))
+    pool_run("varlen16_96_heads", ki.workload_inputs("varlen16"))
+    heads4 = sorted(np.random.default_rng(3).choice(96, 4, replace=False).tolist())
+    for T, name in ((65536, "long_64k_4_heads"), (1048576, "long_1m_4_heads")):
+        x = ki.prefill_inputs([T], H=4, d=128, dtype="bf16", la_law="uniform53", init="normal", seed=3)
+        pool_run(name, x, workers=4)
+        del x
+    # decode: 100 steps of 512 x 96 pairs, 16 processes of 32 sequences
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    procs = [subprocess.Popen([sys.executable, "-c", DECODE_WORKER % ROOT, str(w), "32", "100"],
+                              stdin=subprocess.PIPE, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
+                              env=env) for w in range(16)]
+    try:
+        for p in procs:
+            if p.stdout.readline().strip() != "ready":
+                raise RuntimeError(p.stderr.read()[-2000:])
+        t0 = time.perf_counter()
+        for p in procs:
+            p.stdin.write("go\n")
+            p.stdin.flush()
+        res = [json.loads(p.communicate(timeout=1200)[0].strip().splitlines()[-1]) for p in procs]
+        wall = time.perf_counter() - t0
+    finally:
+        for p in procs:
+            if p.poll() is None:
+                p.kill()
+    ps = sum(r["pair_steps"] for r in res)
+    out["decode_100_steps_512x96"] = {"seconds": round(wall, 3), "pair_steps": ps, "processes": len(procs),
+                                      "pair_steps_per_s": round(ps / wall, 1)}
+    print(f"[cpu-baselines] decode: {out['decode_100_steps_512x96']}", file=sys.stderr, flush=True)
+    return out
 
 
 KERNEL_SOURCES = {
@@ -584,6 +667,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="also time the fp64 oracle beside every workload (several minutes of host time)")
     ap.add_argument("--no-gated", action="store_true", help="skip the timing of the gated entry points")
     ap.add_argument("--no-epilogue", action="store_true",
                     help="skip the timing of the output epilogue and the input prologue")
@@ -726,8 +811,12 @@ def main():
             torch.cuda.empty_cache()
             import gated_delta_rule_09_amd as lib
             res["capacity_split"] = time_split_capacity(args, dev, stream, ki, lib)
+    from gated_delta_rule_09_amd import wait_giveups
+    res["wait_giveups"] = wait_giveups()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
+    if args.cpu_baselines:
+        res["cpu_baselines"] = cpu_baselines()
     print(json.dumps(res), flush=True)
 
 

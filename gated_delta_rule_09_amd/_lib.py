@@ -24,7 +24,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
            4: "KDA_ERR_ALIGN", 5: "KDA_ERR_NO_DEVICE", 6: "KDA_ERR_HIP", 7: "KDA_ERR_VALUE"}
-ABI_VERSION = 3
+ABI_VERSION = 4
 RMS_EPS = 1e-5      # epsilon of the model's RMSNorm
 
 # Every symbol include/kda.h declares, with its ctypes signature.
@@ -33,6 +33,7 @@ SIGNATURES = {
     "kda_abi_version": (ctypes.c_int, []),
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
+    "kda_wait_giveups": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), _I32, _VP]),
     "kda_chunk_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
                                           _VP, _VP, _VP]),
@@ -526,3 +527,17 @@ def kda_decode_step_fused(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tenso
     if st != KDA_OK:
         raise KDAError("kda_decode_step_fused", st)
     return y
+
+
+def wait_giveups(reset: bool = True, device=None) -> int:
+    """Count of bounded in-kernel waits that ran out on the device since the
+    last reset (0 when every wait ended normally); synchronises the current
+    stream."""
+    lib = load()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    n = ctypes.c_uint32(0)
+    with torch.cuda.device(dev):
+        st = lib.kda_wait_giveups(ctypes.byref(n), 1 if reset else 0, _stream_handle(dev))
+    if st != KDA_OK:
+        raise KDAError("kda_wait_giveups", st)
+    return int(n.value)

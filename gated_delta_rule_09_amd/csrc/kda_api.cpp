@@ -75,6 +75,23 @@ const char* kda_status_string(kda_status s) {
 
 const char* kda_last_error(void) { return g_last_error; }
 
+kda_status kda_wait_giveups(uint32_t* count, int32_t reset, void* stream) {
+    if (!count) return KDA_ERR_NULL;
+    kda_status st = check_device();
+    if (st != KDA_OK) return st;
+    hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = kda::read_wait_giveups(count, reset != 0);
+    if (e != hipSuccess) {
+        set_error("kda_wait_giveups", e);
+        return KDA_ERR_HIP;
+    }
+    if (*count != 0)
+        snprintf(g_last_error, sizeof(g_last_error),
+                 "%u bounded in-kernel wait(s) of the prefill ran out: outputs since the last reset are suspect",
+                 *count);
+    return KDA_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -90,7 +107,7 @@ kda_status decode_impl(const char* name, const void* q, const void* k, const voi
                        void* conv_state = nullptr) {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (N < 0 || H < 1 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
-    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (!kda::decode_grid_fits((int64_t)N * H, prologue)) return KDA_ERR_SHAPE;
     if (epilogue && !valid_eps(eps)) return KDA_ERR_VALUE;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !decay || !beta || !state || !o || (gated && !a_log) || (epilogue && !out_gate) ||
@@ -121,10 +138,9 @@ kda_status prefill_impl(const char* name, const void* q, const void* k, const vo
                         int32_t d_v, kda_dtype dtype, void* o, float* final_state, void* stream) {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (N < 1 || H < 1 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
-    if (dtype == KDA_F32 && d_k != 64) return KDA_ERR_SHAPE;
     if (cu_seqlens == nullptr && N != 1) return KDA_ERR_SHAPE;
     if (N > 65535 || H > 65535) return KDA_ERR_SHAPE;   // grid dimensions
-    if ((int64_t)N * H > (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
+    if (!kda::prefill_grid_fits((int64_t)N * H, d_v)) return KDA_ERR_SHAPE;
     if (total_T > 0 && (!q || !k || !v || !decay || !beta || !o || (gated && !a_log))) return KDA_ERR_NULL;
     const void* ptrs[] = {q, k, v, decay, beta, a_log, init_state, cu_seqlens, o, final_state};
     for (const void* p : ptrs)
@@ -181,17 +197,16 @@ kda_status split_impl(const char* name, const void* q, const void* k, const void
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (segments < 1) return KDA_ERR_VALUE;
     if (H < 1 || H > 65535 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
-    if (dtype == KDA_F32 && d_k != 64) return KDA_ERR_SHAPE;
     const SplitPlan p = split_plan(total_T, H, d_k, d_v, dtype, segments);
     if (p.segments == 1)
         return prefill_impl(name, q, k, v, decay, beta, a_log, gated, init_state, nullptr, 1, total_T, H, d_k, d_v,
                             dtype, o, final_state, stream);
-    if ((int64_t)p.segments * H > (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
+    if (!kda::split_grid_fits((int64_t)p.segments * H, (int64_t)(p.segments - 1) * H, d_k, d_v)) return KDA_ERR_SHAPE;
     // The correction addresses 512 tokens of a head with 32-bit byte offsets,
     // and its grid has one workgroup per (head, 512 tokens of a segment).
     const int64_t es = dtype == KDA_BF16 ? 2 : 4;
     if (512 * (int64_t)H * (d_k > d_v ? d_k : d_v) * es > (int64_t)UINT32_MAX) return KDA_ERR_SHAPE;
-    if ((int64_t)H * (p.segments - 1) * ((p.seg_len + 511) / 512) > (int64_t)INT32_MAX) return KDA_ERR_SHAPE;
+    if (!kda::split_correct_grid_fits(H, p.segments, p.seg_len)) return KDA_ERR_SHAPE;
     if (!q || !k || !v || !decay || !beta || !o || (gated && !a_log) || !workspace) return KDA_ERR_NULL;
     const void* ptrs[] = {q, k, v, decay, beta, a_log, init_state, o, final_state, workspace};
     for (const void* ptr : ptrs)
@@ -217,7 +232,7 @@ kda_status split_impl(const char* name, const void* q, const void* k, const void
 kda_status epilogue_checks(const void* o, const void* gate, const float* weight, int64_t rows, int32_t d_v,
                            float eps, kda_dtype dtype, const void* y) {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
-    if (rows < 0 || rows > kda::epilogue_max_rows() || !supported_d(d_v)) return KDA_ERR_SHAPE;
+    if (rows < 0 || !supported_d(d_v) || rows > kda::epilogue_max_rows(dtype == KDA_BF16, d_v)) return KDA_ERR_SHAPE;
     if (!valid_eps(eps)) return KDA_ERR_VALUE;
     if (rows == 0) return KDA_OK;
     if (!o || !gate || !y) return KDA_ERR_NULL;
@@ -396,7 +411,7 @@ kda_status kda_short_conv_prologue(const void* x_q, const void* x_k, const void*
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (N < 1 || H < 1 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
     if (cu_seqlens == nullptr && N != 1) return KDA_ERR_SHAPE;
-    if (H > 65535 || !kda::prologue_grid_fits(total_T, H)) return KDA_ERR_SHAPE;
+    if (H > 65535 || !kda::prologue_grid_fits(N, total_T, H, d_k, d_v, dtype == KDA_BF16)) return KDA_ERR_SHAPE;
     if (total_T > 0 && (!x_q || !x_k || !x_v || !conv_w || !q || !k || !v)) return KDA_ERR_NULL;
     const void* ptrs[] = {x_q, x_k, x_v, conv_w, conv_state_in, cu_seqlens, q, k, v, conv_state_out};
     for (const void* p : ptrs)

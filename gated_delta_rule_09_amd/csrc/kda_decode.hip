@@ -306,6 +306,10 @@ static hipError_t launch_decode_dtype(const DecodeArgs& a) {
     return launch_decode_t<T, 64, 64>(a);
 }
 
+bool decode_grid_fits(int64_t pairs, bool prologue) {
+    return grid_fits(pairs, prologue ? kDecodeThreadsPro : kDecodeThreads);
+}
+
 hipError_t launch_decode(const DecodeArgs& a) {
     return a.bf16 ? launch_decode_dtype<uint16_t>(a) : launch_decode_dtype<float>(a);
 }

@@ -147,18 +147,27 @@ __global__ __launch_bounds__(kEpiThreads) void gate_rmsnorm_kernel(
 }
 
 template <typename T, int DV>
+constexpr int64_t epi_rows_per_block() {
+    return (int64_t)(kEpiThreads / kWave) * (kWave / (DV / Piece<T>::N)) * kEpiRowGroups;
+}
+
+template <typename T, int DV>
 static hipError_t launch_epi_t(const EpilogueArgs& a) {
-    constexpr int VE = Piece<T>::N;
-    constexpr int RPB = (kEpiThreads / kWave) * (kWave / (DV / VE)) * kEpiRowGroups;   // rows per block
+    constexpr int64_t RPB = epi_rows_per_block<T, DV>();
     const int64_t blocks = (a.rows + RPB - 1) / RPB;
     hipLaunchKernelGGL((gate_rmsnorm_kernel<T, DV>), dim3((unsigned)blocks), dim3(kEpiThreads), 0, a.stream,
                        (const u32x4*)a.o, (const u32x4*)a.gate, a.weight, a.rows, a.eps, (u32x4*)a.y);
     return hipGetLastError();
 }
 
-int64_t epilogue_max_rows() {
-    // rows per block is at least 2 (fp32, d_v = 128, one wave, U = 1); the grid is capped at 2^31 - 1 blocks
-    return (int64_t)2 * 0x7fffffff;
+int64_t epilogue_max_rows(bool bf16, int32_t d_v) {
+    // the largest row count whose grid (rows per block x blocks of kEpiThreads) fits a dispatch
+    int64_t rpb;
+    if (bf16) rpb = d_v == 128 ? epi_rows_per_block<uint16_t, 128>() : epi_rows_per_block<uint16_t, 64>();
+    else rpb = d_v == 128 ? epi_rows_per_block<float, 128>() : epi_rows_per_block<float, 64>();
+    int64_t blocks = kMaxGridItems / kEpiThreads;
+    if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
+    return blocks * rpb;
 }
 
 hipError_t launch_epilogue(const EpilogueArgs& a) {

@@ -6,6 +6,14 @@
 
 namespace kda {
 
+// A dispatch's x size is a 32-bit count of work-items, and its block count is
+// at most 2^31 - 1: host validation rejects anything larger before any HIP call.
+constexpr int64_t kMaxGridItems = 0xffffffffll;
+constexpr int64_t kMaxGridBlocks = 0x7fffffffll;
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+    return blocks >= 0 && blocks <= kMaxGridBlocks && blocks * threads <= kMaxGridItems;
+}
+
 // With `gated` set, `log_alpha` points at decay logits z in the element type
 // of q (bf16 or fp32), `beta` at fp32 write-strength logits, and `a_log` at
 // the per-head log-scales A_h [H]; the kernels apply the lower-bounded map
@@ -97,11 +105,22 @@ struct PrologueArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
+bool decode_grid_fits(int64_t pairs, bool prologue);
 hipError_t launch_prologue(const PrologueArgs& p);
-bool prologue_grid_fits(int64_t total_T, int32_t H);
+bool prologue_grid_fits(int64_t N, int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, bool bf16);
 hipError_t launch_epilogue(const EpilogueArgs& a);
-int64_t epilogue_max_rows();
+int64_t epilogue_max_rows(bool bf16, int32_t d_v);
 hipError_t launch_prefill(const PrefillArgs& a);
+// Whether a launch over `units` (sequence, head) pairs at d_v value columns
+// fits a dispatch; for the time split, also the transition job of `trans_units`
+// pairs at d_k columns.
+bool prefill_grid_fits(int64_t units, int32_t d_v);
+bool split_grid_fits(int64_t run_units, int64_t trans_units, int32_t d_k, int32_t d_v);
+bool split_correct_grid_fits(int32_t H, int32_t segments, int64_t seg_len);
+// Bounded in-kernel waits that ran out (a guard against a logic error: each
+// wait's flag is written by a wave that does not wait itself), counted on the
+// current device since the last reset.
+hipError_t read_wait_giveups(uint32_t* count, bool reset);
 // Time split of one sequence (N = 1): the segment runs, then the serial scan
 // over segment end states, then the output correction.
 hipError_t launch_prefill_split_runs(const PrefillArgs& a, const SplitWork& w);

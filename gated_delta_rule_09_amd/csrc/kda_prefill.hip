@@ -72,6 +72,11 @@
 #include "kda_internal.h"
 
 namespace kda {
+
+// Bounded flag waits that ran out on this device (see wait_a); read and reset
+// by the host through read_wait_giveups.
+__device__ uint32_t g_prefill_wait_giveups;
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -365,10 +370,13 @@ __device__ __forceinline__ float lane_elem(const uint32_t (&w)[N], int cc) {
 
 // ---------------------------------------------------------------------------
 // LDS plan.  Two buffers (chunk parity) of the state-independent results that
-// the state-dependent half consumes, plus scratch used only inside SI.
+// the state-dependent half consumes, plus scratch used only inside SI.  fp32
+// operands with d_k = 128 do not fit twice in 160 KB: they get one buffer, and
+// the two roles then take turns on it instead of overlapping.
 // ---------------------------------------------------------------------------
 template <typename OT, int DK>
 struct Plan {
+    static constexpr int NBUF = (sizeof(OT) == 4 && DK == 128) ? 1 : 2;
     static constexpr int ES = sizeof(OT);
     // Row padding, chosen against LDS bank conflicts (32 banks of 4 bytes).
     // The state-dependent waves read 8 bytes from each of 16 consecutive rows
@@ -395,7 +403,7 @@ struct Plan {
     static constexpr int BS = MS + kTiles * 16 * MSTR * 4;         // [4][16] fp32 beta per tile
     static constexpr int BUF = BS + kTiles * 16 * 4;
     // scratch
-    static constexpr int KB = 2 * BUF;                             // [C][LDK]   k * 2^{-x}
+    static constexpr int KB = NBUF * BUF;                          // [C][LDK]   k * 2^{-x}
     static constexpr int FLAG = KB + kC * LDK * ES;                // [4] int: chunk whose A of tile i is ready
     static constexpr int TOTAL = FLAG + 16;
     static_assert(BUF % 16 == 0 && KB % 16 == 0, "alignment");
@@ -564,7 +572,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
 
     // ---- SI: state-independent results of chunk c into buffer (c & 1).  Wave i = tile i.
     auto si = [&](int64_t c) {
-        unsigned char* buf = smem + (c & 1) * PL::BUF;
+        unsigned char* buf = smem + (c % PL::NBUF) * PL::BUF;
         OT* sQE1 = reinterpret_cast<OT*>(buf + PL::QE1);
         OT* sKE1 = reinterpret_cast<OT*>(buf + PL::KE1);
         OT* sKE2 = reinterpret_cast<OT*>(buf + PL::KE2);
@@ -714,7 +722,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     // ---- Inverse of tile ti of chunk c (run by the state-dependent waves, one
     // tile each, on the M and beta the producer waves left in buffer c & 1).
     auto inverse = [&](int64_t c, int ti) {
-        unsigned char* buf = smem + (c & 1) * PL::BUF;
+        unsigned char* buf = smem + (c % PL::NBUF) * PL::BUF;
         OT* sAD = reinterpret_cast<OT*>(buf + PL::AD);
         const float* sMS = reinterpret_cast<const float*>(buf + PL::MS);
         const float* sBS = reinterpret_cast<const float*>(buf + PL::BS);
@@ -764,18 +772,22 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     // Wait until the A of tile i of chunk c is published.  Each flag is written
     // by a wave whose own path up to that write has no waits, so the loop
     // ends; the bound only guards against a logic error.
+    // A wait that runs out is counted in a device word the host can read (the
+    // outputs of that workgroup are then not to be trusted).
     auto wait_a = [&](int64_t c, int i) {
-        for (int spin = 0; spin < (1 << 22); ++spin) {
-            if (__hip_atomic_load(sFLAG + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == (int)c) break;
-            __builtin_amdgcn_s_sleep(1);
+        bool ready = false;
+        for (int spin = 0; spin < (1 << 22) && !ready; ++spin) {
+            ready = __hip_atomic_load(sFLAG + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == (int)c;
+            if (!ready) __builtin_amdgcn_s_sleep(1);
         }
+        if (!ready && lane == 0) atomicAdd(&g_prefill_wait_giveups, 1u);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
     // ---- SD: state-dependent part of chunk c from buffer (c & 1).  Wave w = value columns.
     auto sd = [&](int64_t c, f32x4 (&Sacc)[NCT]) {
         const Rsrc rv_next = v_rsrc(c + 1);
-        const unsigned char* buf = smem + (c & 1) * PL::BUF;
+        const unsigned char* buf = smem + (c % PL::NBUF) * PL::BUF;
         const OT* sQE1 = reinterpret_cast<const OT*>(buf + PL::QE1);
         const OT* sKE1 = reinterpret_cast<const OT*>(buf + PL::KE1);
         const OT* sKE2 = reinterpret_cast<const OT*>(buf + PL::KE2);
@@ -808,14 +820,21 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         // Software pipeline over the tiles: the operands of tile i + 1 are read
         // while tile i computes.  A of tile i is read first (after its flag), so
         // that waiting for it never waits for the prefetch (LDS returns in order).
-        TileOps ops[2];
-        load_ops(0, ops[0]);
+        // fp32 operands with d_k = 128 would need too many registers for two
+        // sets: their tiles read their own operands.
+        constexpr int NOPS = (sizeof(OT) == 4 && DK == 128) ? 1 : 2;
+        TileOps ops[NOPS];
+        if constexpr (NOPS == 2) load_ops(0, ops[0]);
 #pragma unroll
         for (int i = 0; i < kTiles; ++i) {
             if (i != wave - kSIW) wait_a(c, i);
             const Seg aseg = OP::seg(sAD + (16 * i + l16) * PL::LD16);
-            if (i + 1 < kTiles) load_ops(i + 1, ops[(i + 1) & 1]);
-            const TileOps& cur = ops[i & 1];
+            if constexpr (NOPS == 2) {
+                if (i + 1 < kTiles) load_ops(i + 1, ops[(i + 1) & 1]);
+            } else {
+                load_ops(i, ops[0]);
+            }
+            const TileOps& cur = ops[i % NOPS];
             const auto& kseg = cur.kseg;
             const auto& qseg = cur.qseg;
             const auto& eseg = cur.eseg;
@@ -874,6 +893,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             si(0);
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
+                if constexpr (PL::NBUF == 1) __syncthreads();   // the state waves are done with the buffer
                 if (c + 1 < nchunks) si(c + 1);
                 __syncthreads();
             }
@@ -902,6 +922,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
                 sd(c, Sacc);
+                if constexpr (PL::NBUF == 1) __syncthreads();
                 __syncthreads();
             }
         }
@@ -972,6 +993,25 @@ hipError_t launch_split_t(const PrefillArgs& a, const SplitWork& w) {
 
 }  // namespace
 
+bool prefill_grid_fits(int64_t units, int32_t d_v) {
+    return grid_fits(d_v == 128 ? job_blocks<128>(units) : job_blocks<64>(units), 64 * kNW);
+}
+
+bool split_grid_fits(int64_t run_units, int64_t trans_units, int32_t d_k, int32_t d_v) {
+    auto blocks = [](int64_t u, int32_t d) { return d == 128 ? job_blocks<128>(u) : job_blocks<64>(u); };
+    if (d_k == d_v) return grid_fits(blocks(run_units, d_v) + blocks(trans_units, d_k), 64 * kNW);
+    return grid_fits(blocks(run_units, d_v), 64 * kNW) && grid_fits(blocks(trans_units, d_k), 64 * kNW);
+}
+
+hipError_t read_wait_giveups(uint32_t* count, bool reset) {
+    hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_prefill_wait_giveups), sizeof(uint32_t));
+    if (e == hipSuccess && reset) {
+        const uint32_t zero = 0;
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_prefill_wait_giveups), &zero, sizeof(uint32_t));
+    }
+    return e;
+}
+
 template <bool GATED>
 hipError_t launch_prefill_g(const PrefillArgs& a) {
     if (a.bf16) {
@@ -979,7 +1019,8 @@ hipError_t launch_prefill_g(const PrefillArgs& a) {
             return a.d_v == 128 ? launch_t<uint16_t, 128, 128, GATED>(a) : launch_t<uint16_t, 128, 64, GATED>(a);
         return a.d_v == 128 ? launch_t<uint16_t, 64, 128, GATED>(a) : launch_t<uint16_t, 64, 64, GATED>(a);
     }
-    // fp32 operands: d_k = 64 only (the LDS plan of d_k = 128 would exceed 160 KB).
+    if (a.d_k == 128)
+        return a.d_v == 128 ? launch_t<float, 128, 128, GATED>(a) : launch_t<float, 128, 64, GATED>(a);
     return a.d_v == 128 ? launch_t<float, 64, 128, GATED>(a) : launch_t<float, 64, 64, GATED>(a);
 }
 
@@ -995,6 +1036,9 @@ hipError_t launch_split_g(const PrefillArgs& a, const SplitWork& w) {
                                 : launch_split_t<uint16_t, 128, 64, GATED>(a, w);
         return a.d_v == 128 ? launch_split_t<uint16_t, 64, 128, GATED>(a, w) : launch_split_t<uint16_t, 64, 64, GATED>(a, w);
     }
+    if (a.d_k == 128)
+        return a.d_v == 128 ? launch_split_t<float, 128, 128, GATED>(a, w)
+                            : launch_split_t<float, 128, 64, GATED>(a, w);
     return a.d_v == 128 ? launch_split_t<float, 64, 128, GATED>(a, w) : launch_split_t<float, 64, 64, GATED>(a, w);
 }
 

@@ -1,5 +1,6 @@
 // Input prologue of KDA ("Kimi K3 -- Architecture Notes", section 1.1; the
-// atlas's KDA page gives the width): each of the q, k, v projections passes a
+// "Kimi Delta Attention (KDA)" box of the "Kimi K3" visualiser page gives the
+// width): each of the q, k, v projections passes a
 // depthwise causal convolution of width 4 and Swish, and q and k are then
 // L2-normalised over their d_k channels:
 //
@@ -338,9 +339,16 @@ hipError_t launch_dtype(const PrologueArgs& p) {
 
 }  // namespace
 
-bool prologue_grid_fits(int64_t total_T, int32_t H) {
-    // strips * head groups is the grid's x dimension; a head group holds at least one head
-    return (total_T + kStrip - 1) / kStrip * (int64_t)H <= 0x7fffffff;
+bool prologue_grid_fits(int64_t N, int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, bool bf16) {
+    // strips x head groups is the grid's x dimension (one wave per workgroup); a
+    // head group is the heads one wave covers, kWave / (d / elements per lane)
+    const int64_t ve = bf16 ? Pc<uint16_t>::N : Pc<float>::N;
+    const int64_t strips = (total_T + kStrip - 1) / kStrip;
+    for (int32_t d : {d_k, d_v}) {
+        const int64_t per_wave = kWave / (d / ve);
+        if (!grid_fits(strips * ((H + per_wave - 1) / per_wave), kProThreads)) return false;
+    }
+    return grid_fits(N, 256);     // the kernel that passes the states of empty sequences
 }
 
 hipError_t launch_prologue(const PrologueArgs& p) {

@@ -285,6 +285,10 @@ hipError_t correct_t(const PrefillArgs& a, const SplitWork& w) {
 
 }  // namespace
 
+bool split_correct_grid_fits(int32_t H, int32_t segments, int64_t seg_len) {
+    return grid_fits((int64_t)H * (segments - 1) * ((seg_len + kCorrTok - 1) / kCorrTok), kCorrThreads);
+}
+
 hipError_t launch_split_scan(const PrefillArgs& a, const SplitWork& w) {
     if (a.d_k == 128) return a.d_v == 128 ? scan_t<128, 128>(a, w) : scan_t<128, 64>(a, w);
     return a.d_v == 128 ? scan_t<64, 128>(a, w) : scan_t<64, 64>(a, w);
@@ -295,6 +299,7 @@ hipError_t launch_split_correct(const PrefillArgs& a, const SplitWork& w) {
         if (a.d_k == 128) return a.d_v == 128 ? correct_t<uint16_t, 128, 128>(a, w) : correct_t<uint16_t, 128, 64>(a, w);
         return a.d_v == 128 ? correct_t<uint16_t, 64, 128>(a, w) : correct_t<uint16_t, 64, 64>(a, w);
     }
+    if (a.d_k == 128) return a.d_v == 128 ? correct_t<float, 128, 128>(a, w) : correct_t<float, 128, 64>(a, w);
     return a.d_v == 128 ? correct_t<float, 64, 128>(a, w) : correct_t<float, 64, 64>(a, w);
 }
 

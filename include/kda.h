@@ -72,7 +72,7 @@ typedef enum {
 } kda_dtype;
 
 /* Version of this interface; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 int kda_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -82,10 +82,33 @@ const char* kda_status_string(kda_status s);
 const char* kda_last_error(void);
 
 /*
+ * kda_wait_giveups -- count of bounded in-kernel waits that ran out.
+ *
+ * The prefill kernel's state waves wait on a flag in LDS before reading a
+ * triangular inverse that another wave of the workgroup publishes.  Every such
+ * flag is written by a wave whose own path to that write has no waits, so the
+ * wait always ends; its bound (2^22 polls) only guards against a logic error.
+ * A wait that reaches the bound does not hang the GPU: the wave goes on with
+ * whatever the LDS holds and adds one to a counter in device memory, and the
+ * outputs of that launch are then not to be trusted.
+ *
+ *   count  : (host) receives the counter of the current device.
+ *   reset  : non-zero sets the counter back to zero after reading it.
+ *   stream : synchronised before the read (NULL: the default stream).  This
+ *            call blocks the host; it is meant for checks after a batch of
+ *            work, not for every launch.
+ *
+ * Returns KDA_ERR_NULL for a NULL count and KDA_ERR_HIP when the read fails.
+ * A non-zero count returns KDA_OK and also sets kda_last_error's text.
+ */
+kda_status kda_wait_giveups(uint32_t* count, int32_t reset, void* stream);
+
+/*
  * kda_chunk_prefill -- KDA over a packed batch of N sequences.
  *
- * Implements the section-1.1 recurrence chunkwise: "recurrent across chunks and
- * parallel within each chunk" (section 1.2 of the notes), with 64-token chunks
+ * Implements the section-1.1 recurrence chunkwise (section 1.2 of the notes): the
+ * state passes serially from one chunk to the next while the tokens inside a
+ * chunk are processed together, with 64-token chunks
  * split into 16-token tiles whose decay is taken relative to the tile start in
  * log space.  The result equals the token-by-token recurrence up to rounding.
  *
@@ -101,7 +124,7 @@ const char* kda_last_error(void);
  *   N           : number of sequences, >= 1.
  *   total_T     : total tokens, >= 0 (0 copies init to final).
  *   H           : heads, >= 1.
- *   d_k, d_v    : 64 or 128 each.  dtype KDA_F32 requires d_k = 64.
+ *   d_k, d_v    : 64 or 128 each, for both dtypes.
  *   dtype       : element type of q, k, v and o.  The state is always fp32.
  *   o           : [total_T, H, d_v] output (required when total_T > 0).
  *   final_state : [N, H, d_k, d_v] fp32 output, or NULL to skip storing it.
@@ -296,8 +319,8 @@ kda_status kda_decode_step_gated_epilogue(const void* q, const void* k, const vo
                                           void* y, void* stream);
 
 /*
- * Input prologue (section 1.1 of the notes; the width comes from the atlas's
- * KDA page): each of the q, k, v projection outputs passes a depthwise causal
+ * Input prologue (section 1.1 of the notes; the width comes from the "Kimi
+ * Delta Attention (KDA)" box of the "Kimi K3" visualiser page): each of the q, k, v projection outputs passes a depthwise causal
  * convolution of width 4 and Swish, and q and k are then L2-normalised:
  *
  *     conv(x)_t = sum_{j=0..3} w[c, j] x_{t-3+j}[c]   (per head and channel c)

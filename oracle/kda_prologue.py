@@ -9,9 +9,9 @@ What it computes
 ----------------
 "Kimi K3 -- Architecture Notes", section 1.1: the q, k and v projections each
 pass a short convolution and then Swish, and q and k are then L2-normalised.
-The "Kimi Delta Attention" page of the model atlas gives the convolution's
-width (4) and calls it a short convolution over q/k/v that supplies local
-context before the update.  Per head and channel c (a depthwise, causal
+The "Kimi K3" visualiser page (tools/llm-vis), in its "Kimi Delta Attention
+(KDA)" box, gives the convolution's width (4) and calls it a short convolution
+over q/k/v that supplies local context before the update.  Per head and channel c (a depthwise, causal
 convolution; the newest input meets the last tap):
 
     conv(x)_t[c] = sum_{j=0}^{K-1} w[c, j] * x_{t-(K-1)+j}[c],    K = 4,
@@ -26,8 +26,8 @@ its state followed by its inputs.  This is what lets prefill resume and
 decode advance one token at a time.
 
 Readings taken (listed with their reasons in the design notes): the notes'
-order (Swish, then the L2 norm) where the atlas page's listing applies the
-norm first and leaves v without Swish; no convolution bias; eps = 1e-6 inside
+order (Swish, then the L2 norm) where the listing in the visualiser page's KDA
+box applies the norm first and leaves v without Swish; no convolution bias; eps = 1e-6 inside
 the root of the L2 norm; per-head channel order q (d_k), k (d_k), v (d_v) in
 the packed weights and state.
 

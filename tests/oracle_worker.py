@@ -1,13 +1,23 @@
-"""Runs the fp64 oracle on one head's inputs saved as .npy files (test
-infrastructure for the long-context parity test, started as a child process).
+"""Runs the fp64 oracle on one slice of heads saved as .npy files (test
+infrastructure, started as a child process by oracle_pool.py).
 
     python tests/oracle_worker.py <dir>
 
-reads q, k, v, log_alpha [T, 1, d], beta [T, 1], init_state [1, 1, d_k, d_v]
-from <dir>/*.npy and writes o_ref.npy [T, 1, d_v] and final_ref.npy.
+<dir>/meta.json names the entry point ("prefill" or "prefill_gated").  The
+inputs are q, k, v [T, h, d], decay [T, h, d_k] (log alpha, or the decay
+logits of the gated map), beta [T, h] (beta, or its logits), and optionally
+init_state [N, h, d_k, d_v], cu_seqlens [N + 1] and a_log [h] (gated).  A file
+named <name>.bf16.npy holds the raw 16-bit words of a bf16 tensor and is
+widened exactly to fp32 here.  When o_gpu and fin_gpu are present the worker
+compares them with the oracle.  It writes stats.json: the oracle's wall time,
+the token-heads it ran, and max |gpu - ref| and max |ref| for o and the final
+state; with "keep_o_ref" in meta.json it also writes the oracle's o as
+o_ref.npy.
 """
+import json
 import os
 import sys
+import time
 
 import numpy as np
 
@@ -15,11 +25,40 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import oracle  # noqa: E402
 
 
+def load(d: str, name: str):
+    p = os.path.join(d, name + ".npy")
+    if os.path.exists(p):
+        return np.load(p)
+    p = os.path.join(d, name + ".bf16.npy")
+    if os.path.exists(p):
+        return (np.load(p).astype(np.uint32) << 16).view(np.float32)
+    return None
+
+
 def main(d: str):
-    ld = lambda n: np.load(os.path.join(d, n + ".npy"))
-    o, fin = oracle.kda_prefill(ld("q"), ld("k"), ld("v"), ld("log_alpha"), ld("beta"), ld("init_state"))
-    np.save(os.path.join(d, "o_ref.npy"), o)
-    np.save(os.path.join(d, "final_ref.npy"), fin)
+    with open(os.path.join(d, "meta.json")) as f:
+        meta = json.load(f)
+    q, k, v, decay, beta = (load(d, n) for n in ("q", "k", "v", "decay", "beta"))
+    init, cu, a_log = load(d, "init_state"), load(d, "cu_seqlens"), load(d, "a_log")
+    t0 = time.perf_counter()
+    if meta["kind"] == "prefill_gated":
+        o, fin = oracle.kda_prefill_gated(q, k, v, decay, a_log, beta, init, cu)
+    else:
+        o, fin = oracle.kda_prefill(q, k, v, decay, beta, init, cu)
+    stats = {"seconds": time.perf_counter() - t0, "token_heads": int(q.shape[0] * q.shape[1]),
+             "o_ref_max": float(np.abs(o).max()) if o.size else 0.0,
+             "f_ref_max": float(np.abs(fin).max()) if fin.size else 0.0}
+    o_gpu, f_gpu = load(d, "o_gpu"), load(d, "fin_gpu")
+    if o_gpu is not None:
+        stats["o_err_max"] = float(np.abs(o_gpu.astype(np.float64) - o).max()) if o.size else 0.0
+        stats["o_finite"] = bool(np.isfinite(o_gpu).all())
+    if f_gpu is not None:
+        stats["f_err_max"] = float(np.abs(f_gpu.astype(np.float64) - fin).max()) if fin.size else 0.0
+        stats["f_finite"] = bool(np.isfinite(f_gpu).all())
+    if meta.get("keep_o_ref"):
+        np.save(os.path.join(d, "o_ref.npy"), o)
+    with open(os.path.join(d, "stats.json"), "w") as f:
+        json.dump(stats, f)
 
 
 if __name__ == "__main__":

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.kda_abi_version() == L.ABI_VERSION == 3
+    assert lib.kda_abi_version() == L.ABI_VERSION == 4
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -60,7 +60,7 @@ def decode(lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dt=7), 3), (dict(dk=96), 2), (dict(dv=32), 2), (dict(H=0), 2), (dict(N=0), 2),
-    (dict(T=-1), 2), (dict(N=2), 2), (dict(dt=L.KDA_F32, dk=128), 2), (dict(N=70000, cu=P), 2),
+    (dict(T=-1), 2), (dict(N=2), 2), (dict(N=70000, cu=P), 2),
     (dict(q=None), 1), (dict(b=None), 1), (dict(o=None), 1), (dict(la=MIS), 4), (dict(fin=MIS), 4),
     (dict(init=MIS), 4), (dict(cu=MIS, N=1), 4),
 ])
@@ -92,7 +92,7 @@ def decode_gated(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dt=7), 3), (dict(dk=96), 2), (dict(N=2), 2), (dict(dt=L.KDA_F32, dk=128), 2),
+    (dict(dt=7), 3), (dict(dk=96), 2), (dict(N=2), 2),
     (dict(z=None), 1), (dict(A=None), 1), (dict(b=None), 1), (dict(A=MIS), 4), (dict(z=MIS), 4),
 ])
 def test_gated_prefill_rejects_bad_arguments_before_touching_the_device(kw, code):
@@ -259,7 +259,7 @@ def prefill_gated_split(lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dt=7), 3), (dict(seg=0), 7), (dict(seg=-3), 7), (dict(dk=96), 2), (dict(H=0), 2), (dict(T=-1), 2),
-    (dict(H=70000), 2), (dict(dt=L.KDA_F32, dk=128), 2), (dict(ws=None), 1), (dict(q=None), 1), (dict(o=None), 1),
+    (dict(H=70000), 2), (dict(ws=None), 1), (dict(q=None), 1), (dict(o=None), 1),
     (dict(ws=MIS), 4), (dict(la=MIS), 4), (dict(init=MIS), 4), (dict(wsb=1000), 7),
     (dict(H=40000, dk=128, dv=128), 2), (dict(H=20000, dk=64, dv=128, dt=L.KDA_F32), 2),
     # one segment is the plain prefill: its own checks apply and no workspace is needed
@@ -329,3 +329,82 @@ def test_split_binding_checks_before_calling_the_library():
     assert L.split_workspace_bytes(T, H, d, d, torch.bfloat16, 2) == \
         lib.kda_split_workspace_bytes(T, H, d, d, L.KDA_BF16, 2) > 0
     assert L.split_workspace_bytes(T, H, d, d, torch.float32, 1) == 0
+
+
+# ---- sizes at the edge of one dispatch (blocks x threads < 2^32, blocks < 2^31) ----
+
+OK_OR_NO_DEVICE = (0, 5)    # validation passed: 0 with a device, 5 without one
+
+
+def test_fp32_dk128_is_accepted():
+    lib = L.load()
+    for dv in (64, 128):
+        assert prefill(lib, dt=L.KDA_F32, dk=128, dv=dv) in OK_OR_NO_DEVICE
+        assert prefill_gated(lib, dt=L.KDA_F32, dk=128, dv=dv) in OK_OR_NO_DEVICE
+        assert prefill_split(lib, dt=L.KDA_F32, dk=128, dv=dv) in OK_OR_NO_DEVICE
+
+
+def test_decode_grid_limit():
+    """1024 threads per (sequence, head) pair: at most 4,194,303 pairs; 512 with the prologue."""
+    lib = L.load()
+    assert decode(lib, N=65535, H=64) in OK_OR_NO_DEVICE           # 4,194,240 pairs
+    assert decode(lib, N=65536, H=64) == 2                         # 4,194,304 pairs
+    assert decode_fused(lib, N=65536, H=64) in OK_OR_NO_DEVICE     # 512 threads per pair
+    assert decode_fused(lib, N=65536, H=128) == 2                  # 8,388,608 pairs
+
+
+def test_prefill_grid_limit():
+    """512 threads per workgroup; one workgroup per (sequence, head) pair at d_v = 64,
+    two per pair (padded to groups of 16) at d_v = 128."""
+    lib = L.load()
+    assert prefill(lib, N=65535, H=128, cu=P, dv=64) in OK_OR_NO_DEVICE     # 8,388,480 workgroups
+    assert prefill(lib, N=65535, H=129, cu=P, dv=64) == 2                   # 8,454,015
+    assert prefill(lib, N=65535, H=64, cu=P, dv=128) in OK_OR_NO_DEVICE     # 8,388,480
+    assert prefill(lib, N=65535, H=65, cu=P, dv=128) == 2
+
+
+def test_split_grid_limits():
+    """The segment runs and transitions share one launch when d_v = d_k; the
+    correction has one 512-thread workgroup per (head, segment, 512 tokens)."""
+    lib = L.load()
+    # 2 segments x 65535 heads: runs + transitions = 3 x 65535 units x 2 workgroups each
+    assert prefill_split(lib, H=65535, dk=128, dv=128, T=4096, seg=2) == 2
+    assert prefill_split(lib, H=30000, dk=64, dv=64, T=4096, seg=2) in OK_OR_NO_DEVICE
+    # correction: H * (segments - 1) * ceil(seg_len / 512) workgroups of 512 threads
+    # (65535 heads x 128 blocks of 512 tokens fit; x 129 do not)
+    assert prefill_split(lib, H=65535, dk=64, dv=64, T=2 * 65536, seg=2) in OK_OR_NO_DEVICE
+    assert prefill_split(lib, H=65535, dk=64, dv=64, T=2 * 65600, seg=2) == 2
+
+
+def test_epilogue_grid_limit():
+    """One 64-thread workgroup per 4 rows (bf16, d_v = 128) or 2 rows (fp32, d_v = 128)."""
+    lib = L.load()
+    per_block = {(L.KDA_BF16, 128): 4, (L.KDA_F32, 128): 2, (L.KDA_BF16, 64): 8, (L.KDA_F32, 64): 4}
+    for (dt, dv), rpb in per_block.items():
+        limit = rpb * ((2 ** 32 - 1) // 64)
+        assert epilogue(lib, dt=dt, dv=dv, rows=limit) in OK_OR_NO_DEVICE
+        assert epilogue(lib, dt=dt, dv=dv, rows=limit + 1) == 2
+
+
+def test_prologue_grid_limit():
+    """One 64-thread workgroup per 16 tokens of a group of heads (4 heads per group at
+    bf16 and d = 128, 2 at fp32 and d = 128)."""
+    lib = L.load()
+    strips = (2 ** 32 - 1) // 64
+    assert prologue(lib, dk=128, dv=128, H=4, T=16 * strips) in OK_OR_NO_DEVICE
+    assert prologue(lib, dk=128, dv=128, H=5, T=16 * strips) == 2
+    assert prologue(lib, dk=128, dv=128, H=4, T=16 * strips, dt=L.KDA_F32) == 2
+    assert prologue(lib, dk=128, dv=128, H=2, T=16 * strips, dt=L.KDA_F32) in OK_OR_NO_DEVICE
+
+
+def test_wait_giveups_host_path():
+    """The give-up counter's query: a NULL output is rejected before any HIP call;
+    without a device it reports no device."""
+    lib = L.load()
+    assert lib.kda_wait_giveups(None, 0, None) == 1
+    n = ctypes.c_uint32(7)
+    st = lib.kda_wait_giveups(ctypes.byref(n), 1, None)
+    if _has_gpu():
+        assert st == 0
+    else:
+        assert st == 5 and n.value == 7

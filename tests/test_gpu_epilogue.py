@@ -9,8 +9,8 @@ import torch
 import kda_inputs as ki
 import oracle
 from gpu_util import TOL, announce, device, host, rel_err
-from gated_delta_rule_09_amd import (RMS_EPS, kda_chunk_prefill_gated, kda_chunk_prefill_gated_epilogue,
-                                     kda_decode_step_gated, kda_decode_step_gated_epilogue, kda_output_gate_rmsnorm)
+from gated_delta_rule_09_amd import (RMS_EPS, kda_chunk_prefill_gated_epilogue, kda_decode_step_gated_epilogue,
+                                     kda_output_gate_rmsnorm)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,58 +90,65 @@ def test_epilogue_long_64k_sampled_rows():
     assert bool(torch.isfinite(y).all())
 
 
-def check_through_norm(y, y_ref, o_gpu, o_ref, weight, dtype, what):
-    """y of a fused entry point against the oracle, with the error of the o it
-    normalised carried through the norm.
+def check_through_norm(y, y_ref, o_ref, weight, dtype, what):
+    """y of a fused entry point against the oracle, with the o tolerance
+    carried through the norm.
 
-    o_gpu is the output of the matching unfused entry point on the same
-    inputs, held to the suite's o tolerance here; it only sizes the error
-    budget.  With s(o) = sqrt(mean(o^2) + eps), the map f(o) = o / s(o)
-    satisfies |f(o) - f(o_ref)|_2 <= 2 |o - o_ref|_2 / s(o_ref) for every o
-    (s is 1/sqrt(d)-Lipschitz and |o|_2 <= sqrt(d) s(o)); the gate and the gain
+    The budget comes from the oracle and the stated tolerances only: the o the
+    fused kernel normalises is held to the suite's o tolerance, max|o - o_ref|
+    <= TOL max|o_ref| over the tensor, so each row of d_v values is within
+    sqrt(d_v) TOL max|o_ref| of o_ref in the 2-norm.  With s(o) =
+    sqrt(mean(o^2) + eps), the map f(o) = o / s(o) satisfies
+    |f(o) - f(o_ref)|_2 <= 2 |o - o_ref|_2 / s(o_ref) for every o (s is
+    1/sqrt(d)-Lipschitz and |o|_2 <= sqrt(d) s(o)); the gate and the gain
     scale each channel by at most max|w|, and rounding y to the working dtype
-    adds u |y|.  The o the fused kernel normalises differs from the stored
-    o_gpu by at most the output rounding (u |o_gpu|), so each row must satisfy
-        |y - y_ref|_2 <= (1 + u) 2 max|w| (|o_gpu - o_ref|_2 + u |o_gpu|_2) / s(o_ref)
+    adds u |y|.  So each row must satisfy
+        |y - y_ref|_2 <= (1 + u) 2 max|w| sqrt(d_v) TOL max|o_ref| / s(o_ref)
                          + (u + 1e-6) |y_ref|_2.
-    A row whose o is small next to the rest is ill-conditioned (the norm
-    magnifies its absolute error by 1 / s), and only such rows get a budget
-    much wider than u."""
+    A row whose o is small next to the rest of the tensor is ill-conditioned
+    (the norm magnifies its absolute error by 1 / s), and only such rows get
+    a budget much wider than u."""
     y = np.asarray(y, np.float64)
-    o_gpu = np.asarray(o_gpu, np.float64)
-    eo = rel_err(o_gpu, o_ref)
-    assert eo <= TOL[dtype], f"{what}: o rel err {eo}"
     u = ELEM_TOL[dtype]
+    d_v = o_ref.shape[-1]
     wmax = 1.0 if weight is None else float(np.abs(weight).max())
     nrm = lambda a: np.sqrt(np.sum(a * a, axis=-1))
+    e_o = np.sqrt(d_v) * TOL[dtype] * float(np.abs(o_ref).max())
     s_ref = np.sqrt(np.mean(o_ref * o_ref, axis=-1) + RMS_EPS)
     err = nrm(y - y_ref)
-    bound = ((1 + u) * 2.0 * wmax * (nrm(o_gpu - o_ref) + u * nrm(o_gpu)) / s_ref + (u + 1e-6) * nrm(y_ref))
+    bound = (1 + u) * 2.0 * wmax * e_o / s_ref + (u + 1e-6) * nrm(y_ref)
     ratio = err / bound
     i = np.unravel_index(np.argmax(ratio), ratio.shape)
-    announce(f"  {what}: o rel err {eo:.3e}; y norm-wise rel err {rel_err(y, y_ref):.3e}; worst row "
+    tight = s_ref >= 2.0 * wmax * e_o / np.sqrt(d_v)      # rows whose budget is below |y| itself
+    announce(f"  {what}: y norm-wise rel err {rel_err(y, y_ref):.3e}; worst row "
              f"{tuple(int(j) for j in i)}: |dy| {err[i]:.3e} of budget {bound[i]:.3e} (row rms {s_ref[i]:.3e}, "
-             f"max|o| {np.abs(o_ref).max():.3e}); median |dy|/|y| {np.median(err / nrm(y_ref)):.2e}")
+             f"max|o| {np.abs(o_ref).max():.3e}); median |dy|/|y| {np.median(err / nrm(y_ref)):.2e}; "
+             f"{100.0 * tight.mean():.0f}% of rows held below |y|")
     assert np.isfinite(y).all()
-    assert (ratio <= 1.0).all(), f"{what}: y beyond the error carried from o"
+    assert (ratio <= 1.0).all(), f"{what}: y beyond the o tolerance carried through the norm"
 
 
-def check_prefill_epilogue(x, og, dtype, heads=None, what=""):
+def check_prefill_epilogue(x, og, dtype, heads=None, what="", pool=False):
     announce(f"prefill+epilogue {what}: lengths={x.lengths[:4]}{'...' if len(x.lengths) > 4 else ''} "
              f"H={x.q.shape[1]} d_k={x.q.shape[2]} d_v={x.v.shape[2]} {dtype}")
     y, fin = kda_chunk_prefill_gated_epilogue(x.q, x.k, x.v, x.g_logits, x.a_log, x.beta_logits, og["gate"],
                                               og["weight"], init_state=x.init_state, cu_seqlens=x.cu_seqlens)
-    o_gpu, _ = kda_chunk_prefill_gated(x.q, x.k, x.v, x.g_logits, x.a_log, x.beta_logits, x.init_state,
-                                       x.cu_seqlens, output_final_state=False)
     torch.cuda.synchronize()
     hs = slice(None) if heads is None else list(heads)
-    o_ref, f_ref = oracle.kda_prefill_gated(host(x.q), host(x.k), host(x.v), host(x.g_logits), host(x.a_log),
-                                            host(x.beta_logits), host(x.init_state), host(x.cu_seqlens),
-                                            heads=heads)
+    if pool:
+        # every head (or `heads`), the oracle fanned out over child processes
+        import oracle_pool
+        r = oracle_pool.prefill(x.q, x.k, x.v, x.g_logits, x.beta_logits, x.init_state, x.cu_seqlens,
+                                a_log=x.a_log, fin_gpu=fin, heads=heads, progress=announce, return_o_ref=True)
+        o_ref, ef = r["o_ref"], r["rel_f"]
+    else:
+        o_ref, f_ref = oracle.kda_prefill_gated(host(x.q), host(x.k), host(x.v), host(x.g_logits), host(x.a_log),
+                                                host(x.beta_logits), host(x.init_state), host(x.cu_seqlens),
+                                                heads=heads)
+        ef = rel_err(host(fin)[:, hs], f_ref)
     y_ref = oracle.kda_output_gate_rmsnorm(o_ref, host(og["gate"])[:, hs], host(og["weight"]), RMS_EPS)
-    ef = rel_err(host(fin)[:, hs], f_ref)
     announce(f"  rel err final={ef:.3e} (tol {TOL[dtype]})")
-    check_through_norm(host(y)[:, hs], y_ref, host(o_gpu)[:, hs], o_ref, host(og["weight"]), dtype, "y")
+    check_through_norm(host(y)[:, hs], y_ref, o_ref, host(og["weight"]), dtype, "y")
     assert ef <= TOL[dtype]
 
 
@@ -155,11 +162,10 @@ def test_prefill_epilogue_ragged(lengths, dtype):
     check_prefill_epilogue(x, og, dtype, what=f"ragged {lengths}")
 
 
-def test_prefill_epilogue_bf16_4k_sampled_heads():
+def test_prefill_epilogue_bf16_4k_all_heads():
     x = ki.gated_inputs([4096], H=96, d=128, dtype="bf16", seed=41, device=device())
     og = ki.out_gate_inputs((4096, 96, 128), "bf16", seed=41, device=device())
-    check_prefill_epilogue(x, og, "bf16", heads=np.random.default_rng(41).choice(96, 4, replace=False),
-                           what="bf16 4K")
+    check_prefill_epilogue(x, og, "bf16", what="bf16 4K, all heads", pool=True)
 
 
 def test_prefill_epilogue_long_64k_two_heads():
@@ -180,16 +186,13 @@ def test_decode_epilogue_steps(dtype, d, d_v):
         x = ki.decode_gated_inputs(N, H, d, dtype=dtype, seed=43, step=step, device=device(), d_v=d_v)
         og = ki.out_gate_inputs((N, H, d_v), dtype, seed=43, step=step, device=device())
         w = og["weight"] if step % 2 == 0 else None
-        o_gpu = kda_decode_step_gated(x["q"], x["k"], x["v"], x["g_logits"], x["a_log"], x["beta_logits"],
-                                      state.clone())
         y = kda_decode_step_gated_epilogue(x["q"], x["k"], x["v"], x["g_logits"], x["a_log"], x["beta_logits"],
                                            og["gate"], state, norm_weight=w)
         torch.cuda.synchronize()
         o_ref, ref = oracle.kda_decode_step_gated(host(x["q"]), host(x["k"]), host(x["v"]), host(x["g_logits"]),
                                                   host(x["a_log"]), host(x["beta_logits"]), ref)
         y_ref = oracle.kda_output_gate_rmsnorm(o_ref, host(og["gate"]), None if w is None else host(w), RMS_EPS)
-        check_through_norm(host(y), y_ref, host(o_gpu), o_ref, None if w is None else host(w), dtype,
-                           f"step {step}")
+        check_through_norm(host(y), y_ref, o_ref, None if w is None else host(w), dtype, f"step {step}")
     es = rel_err(host(state), ref)
     announce(f"  rel err state={es:.3e}")
     assert es <= TOL[dtype]
@@ -206,16 +209,13 @@ def test_decode_epilogue_full_shape_sampled_pairs():
     for step in range(3):
         x = ki.decode_gated_inputs(N, H, d, "bf16", seed=44, step=step, device=device())
         og = ki.out_gate_inputs((N, H, d), "bf16", seed=44, step=step, device=device())
-        o_gpu = kda_decode_step_gated(x["q"], x["k"], x["v"], x["g_logits"], x["a_log"], x["beta_logits"],
-                                      state.clone())
         y = kda_decode_step_gated_epilogue(x["q"], x["k"], x["v"], x["g_logits"], x["a_log"], x["beta_logits"],
                                            og["gate"], state, norm_weight=og["weight"])
         sel = {kk: host(vv[ns, hs])[None] for kk, vv in x.items() if kk != "a_log"}
         o_ref, ref = oracle.kda_decode_step_gated(sel["q"], sel["k"], sel["v"], sel["g_logits"],
                                                   host(x["a_log"])[flat % H], sel["beta_logits"], ref)
         y_ref = oracle.kda_output_gate_rmsnorm(o_ref, host(og["gate"][ns, hs])[None], host(og["weight"]), RMS_EPS)
-        check_through_norm(host(y[ns, hs])[None], y_ref, host(o_gpu[ns, hs])[None], o_ref, host(og["weight"]),
-                           "bf16", f"step {step}")
+        check_through_norm(host(y[ns, hs])[None], y_ref, o_ref, host(og["weight"]), "bf16", f"step {step}")
     torch.cuda.synchronize()
     es = rel_err(host(state[ns, hs])[None], ref)
     announce(f"  state rel err {es:.3e}")

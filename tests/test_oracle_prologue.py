@@ -1,6 +1,7 @@
 """Pins for the fp64 input-prologue oracle ("Kimi K3 -- Architecture Notes",
 section 1.1: the q/k/v projections pass a short convolution and Swish, then q
-and k are L2-normalised; the atlas's KDA page: convolution width 4), and
+and k are L2-normalised; the "Kimi Delta Attention (KDA)" box of the "Kimi K3"
+visualiser page: convolution width 4), and
 mutants that the pins must reject.
 
 The pins are closed forms and structural facts that hold however the oracle
