@@ -41,6 +41,39 @@ template <> struct Elem<uint16_t> {   // bf16 stored as raw 16-bit words
     static __device__ __forceinline__ void store(uint16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
 };
 
+// Value of lane Q of this lane's quad (DPP quad_perm broadcast).
+template <int Q>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x55 * Q, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float quad_bcast(float v, int q) {   // q is a constant after unrolling
+    switch (q) {
+        case 0: return quad_bcast<0>(v);
+        case 1: return quad_bcast<1>(v);
+        case 2: return quad_bcast<2>(v);
+        default: return quad_bcast<3>(v);
+    }
+}
+
+// Value of lane K of this lane's 16-lane row (DPP row_newbcast, gfx90a and
+// later); folded by the compiler into the consuming VALU instruction.
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_bcast(float v, int k) {   // k is a constant after unrolling
+    switch (k) {
+        case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
+        case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
+        case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
+        case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
+        case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
+        case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
+        case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
+        case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
+    }
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);

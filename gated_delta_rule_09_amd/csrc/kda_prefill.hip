@@ -114,39 +114,6 @@ __device__ __forceinline__ LoHi block_pair(float v) {
     }
 }
 
-// Value of lane Q of this lane's quad (DPP quad_perm broadcast).
-template <int Q>
-__device__ __forceinline__ float quad_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x55 * Q, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float quad_bcast(float v, int q) {   // q is a constant after unrolling
-    switch (q) {
-        case 0: return quad_bcast<0>(v);
-        case 1: return quad_bcast<1>(v);
-        case 2: return quad_bcast<2>(v);
-        default: return quad_bcast<3>(v);
-    }
-}
-
-// Value of lane K of this lane's 16-lane row (DPP row_newbcast, gfx90a and
-// later); folded by the compiler into the consuming VALU instruction.
-template <int K>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row_bcast(float v, int k) {   // k is a constant after unrolling
-    switch (k) {
-        case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
-        case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
-        case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
-        case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
-        case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
-        case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
-        case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
-        case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
-    }
-}
-
 // Order this wave's earlier LDS writes before its later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
@@ -1015,9 +982,8 @@ hipError_t read_wait_giveups(uint32_t* count, bool reset) {
 template <bool GATED>
 hipError_t launch_prefill_g(const PrefillArgs& a) {
     if (a.bf16) {
-        if (a.d_k == 128)
-            return a.d_v == 128 ? launch_t<uint16_t, 128, 128, GATED>(a) : launch_t<uint16_t, 128, 64, GATED>(a);
-        return a.d_v == 128 ? launch_t<uint16_t, 64, 128, GATED>(a) : launch_t<uint16_t, 64, 64, GATED>(a);
+        const PrefillJob j0{a.v, a.init_state, a.cu_seqlens, a.o, a.final_state, 0, 0, 0, a.N * a.H, 0, kInitAll};
+        return launch_chunk_jobs(a, a.d_v, j0, PrefillJob{});
     }
     if (a.d_k == 128)
         return a.d_v == 128 ? launch_t<float, 128, 128, GATED>(a) : launch_t<float, 128, 64, GATED>(a);
@@ -1031,10 +997,14 @@ hipError_t launch_prefill(const PrefillArgs& a) {
 template <bool GATED>
 hipError_t launch_split_g(const PrefillArgs& a, const SplitWork& w) {
     if (a.bf16) {
-        if (a.d_k == 128)
-            return a.d_v == 128 ? launch_split_t<uint16_t, 128, 128, GATED>(a, w)
-                                : launch_split_t<uint16_t, 128, 64, GATED>(a, w);
-        return a.d_v == 128 ? launch_split_t<uint16_t, 64, 128, GATED>(a, w) : launch_split_t<uint16_t, 64, 64, GATED>(a, w);
+        const PrefillJob run{a.v, a.init_state, nullptr, a.o, w.ends, w.seg_len, 0, 0, w.segments * a.H, 0,
+                             kInitFirst};
+        const PrefillJob trans{nullptr, nullptr, nullptr, w.qt, w.phis, w.seg_len, w.seg_len, 1,
+                               (w.segments - 1) * a.H, 0, kInitIdentity};
+        if (a.d_v == a.d_k) return launch_chunk_jobs(a, a.d_v, run, trans);
+        hipError_t e = launch_chunk_jobs(a, a.d_v, run, PrefillJob{});
+        if (e != hipSuccess) return e;
+        return launch_chunk_jobs(a, a.d_k, trans, PrefillJob{});
     }
     if (a.d_k == 128)
         return a.d_v == 128 ? launch_split_t<float, 128, 128, GATED>(a, w)
