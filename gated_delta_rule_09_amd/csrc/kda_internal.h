@@ -111,9 +111,6 @@ bool prologue_grid_fits(int64_t N, int64_t total_T, int32_t H, int32_t d_k, int3
 hipError_t launch_epilogue(const EpilogueArgs& a);
 int64_t epilogue_max_rows(bool bf16, int32_t d_v);
 hipError_t launch_prefill(const PrefillArgs& a);
-// bf16 prefill jobs (kda_chunk.hip): the state advances once per 64-token
-// chunk; d_v is the value width of the jobs (d_k for transition jobs).
-hipError_t launch_chunk_jobs(const PrefillArgs& a, int d_v, const PrefillJob& j0, const PrefillJob& j1);
 // Whether a launch over `units` (sequence, head) pairs at d_v value columns
 // fits a dispatch; for the time split, also the transition job of `trans_units`
 // pairs at d_k columns.

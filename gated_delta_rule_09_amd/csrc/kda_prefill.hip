@@ -982,8 +982,9 @@ hipError_t read_wait_giveups(uint32_t* count, bool reset) {
 template <bool GATED>
 hipError_t launch_prefill_g(const PrefillArgs& a) {
     if (a.bf16) {
-        const PrefillJob j0{a.v, a.init_state, a.cu_seqlens, a.o, a.final_state, 0, 0, 0, a.N * a.H, 0, kInitAll};
-        return launch_chunk_jobs(a, a.d_v, j0, PrefillJob{});
+        if (a.d_k == 128)
+            return a.d_v == 128 ? launch_t<uint16_t, 128, 128, GATED>(a) : launch_t<uint16_t, 128, 64, GATED>(a);
+        return a.d_v == 128 ? launch_t<uint16_t, 64, 128, GATED>(a) : launch_t<uint16_t, 64, 64, GATED>(a);
     }
     if (a.d_k == 128)
         return a.d_v == 128 ? launch_t<float, 128, 128, GATED>(a) : launch_t<float, 128, 64, GATED>(a);
@@ -997,14 +998,10 @@ hipError_t launch_prefill(const PrefillArgs& a) {
 template <bool GATED>
 hipError_t launch_split_g(const PrefillArgs& a, const SplitWork& w) {
     if (a.bf16) {
-        const PrefillJob run{a.v, a.init_state, nullptr, a.o, w.ends, w.seg_len, 0, 0, w.segments * a.H, 0,
-                             kInitFirst};
-        const PrefillJob trans{nullptr, nullptr, nullptr, w.qt, w.phis, w.seg_len, w.seg_len, 1,
-                               (w.segments - 1) * a.H, 0, kInitIdentity};
-        if (a.d_v == a.d_k) return launch_chunk_jobs(a, a.d_v, run, trans);
-        hipError_t e = launch_chunk_jobs(a, a.d_v, run, PrefillJob{});
-        if (e != hipSuccess) return e;
-        return launch_chunk_jobs(a, a.d_k, trans, PrefillJob{});
+        if (a.d_k == 128)
+            return a.d_v == 128 ? launch_split_t<uint16_t, 128, 128, GATED>(a, w)
+                                : launch_split_t<uint16_t, 128, 64, GATED>(a, w);
+        return a.d_v == 128 ? launch_split_t<uint16_t, 64, 128, GATED>(a, w) : launch_split_t<uint16_t, 64, 64, GATED>(a, w);
     }
     if (a.d_k == 128)
         return a.d_v == 128 ? launch_split_t<float, 128, 128, GATED>(a, w)
