@@ -26,6 +26,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE
            4: "KDA_ERR_ALIGN", 5: "KDA_ERR_NO_DEVICE", 6: "KDA_ERR_HIP", 7: "KDA_ERR_VALUE"}
 ABI_VERSION = 4
 RMS_EPS = 1e-5      # epsilon of the model's RMSNorm
+SPLIT_SCRATCH_BYTES = 64 << 20   # KDA_SPLIT_SCRATCH_BYTES: the no-alloc split's scratch per device
 
 # Every symbol include/kda.h declares, with its ctypes signature.
 _VP, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -59,6 +60,8 @@ SIGNATURES = {
     "kda_chunk_prefill_gated_split": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32,
                                                       ctypes.c_int, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "kda_split_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32, ctypes.c_int, _I32]),
+    "kda_chunk_prefill_split_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32,
+                                                        ctypes.c_int, _I32, _VP, _VP, _VP]),
     "kda_split_segments": (_I32, [_I64, _I32, _I32, _I32, _I32]),
 }
 
@@ -248,7 +251,7 @@ def split_workspace_bytes(total_T: int, H: int, d_k: int, d_v: int, dtype: torch
 
 
 def _split_call(name: str, q, k, v, decay, decay_dtype, a_log, beta, init_state, segments, workspace, o,
-                final_state, output_final_state):
+                final_state, output_final_state, noalloc=False):
     lib = load()
     T, H, d_k = q.shape
     d_v = v.shape[2]
@@ -274,6 +277,12 @@ def _split_call(name: str, q, k, v, decay, decay_dtype, a_log, beta, init_state,
     if final_state is not None:
         _check(final_state, "final_state", (1, H, d_k, d_v), torch.float32, dev)
     need = int(lib.kda_split_workspace_bytes(T, H, d_k, d_v, code, int(segments)))
+    if noalloc:
+        st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), _ptr(init_state), T, H, d_k,
+                                d_v, code, int(segments), _ptr(o), _ptr(final_state), _stream_handle(dev))
+        if st != KDA_OK:
+            raise KDAError(name, st)
+        return o, final_state
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -304,6 +313,20 @@ def kda_chunk_prefill_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     bytes).  Returns (o, final_state) with final_state [1, H, d_k, d_v]."""
     return _split_call("kda_chunk_prefill_split", q, k, v, log_alpha, torch.float32, None, beta, init_state,
                        segments, workspace, o, final_state, output_final_state)
+
+
+def kda_chunk_prefill_split_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                    log_alpha: torch.Tensor, beta: torch.Tensor,
+                                    init_state: Optional[torch.Tensor] = None,
+                                    segments: Optional[int] = None,
+                                    o: Optional[torch.Tensor] = None,
+                                    final_state: Optional[torch.Tensor] = None,
+                                    output_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The time-split prefill on the library's own scratch (include/kda.h,
+    kda_chunk_prefill_split_noalloc): the C call allocates nothing.  Pass o and
+    final_state to keep this wrapper from allocating them."""
+    return _split_call("kda_chunk_prefill_split_noalloc", q, k, v, log_alpha, torch.float32, None, beta, init_state,
+                       segments, None, o, final_state, output_final_state, noalloc=True)
 
 
 def kda_chunk_prefill_gated_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -190,10 +190,12 @@ SplitPlan split_plan(int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, kda_d
     return p;
 }
 
+// `noalloc`: the workspace is the library's own scratch (workspace and
+// workspace_bytes are ignored); a plan larger than it is rejected.
 kda_status split_impl(const char* name, const void* q, const void* k, const void* v, const void* decay,
                       const float* beta, const float* a_log, bool gated, const float* init_state, int64_t total_T,
                       int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype, int32_t segments, void* workspace,
-                      size_t workspace_bytes, void* o, float* final_state, void* stream) {
+                      size_t workspace_bytes, void* o, float* final_state, void* stream, bool noalloc = false) {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (segments < 1) return KDA_ERR_VALUE;
     if (H < 1 || H > 65535 || total_T < 0 || !supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_SHAPE;
@@ -207,13 +209,26 @@ kda_status split_impl(const char* name, const void* q, const void* k, const void
     const int64_t es = dtype == KDA_BF16 ? 2 : 4;
     if (512 * (int64_t)H * (d_k > d_v ? d_k : d_v) * es > (int64_t)UINT32_MAX) return KDA_ERR_SHAPE;
     if (!kda::split_correct_grid_fits(H, p.segments, p.seg_len)) return KDA_ERR_SHAPE;
-    if (!q || !k || !v || !decay || !beta || !o || (gated && !a_log) || !workspace) return KDA_ERR_NULL;
-    const void* ptrs[] = {q, k, v, decay, beta, a_log, init_state, o, final_state, workspace};
+    if (!q || !k || !v || !decay || !beta || !o || (gated && !a_log) || (!noalloc && !workspace)) return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, decay, beta, a_log, init_state, o, final_state, noalloc ? nullptr : workspace};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return KDA_ERR_ALIGN;
-    if (workspace_bytes < p.bytes) return KDA_ERR_VALUE;
+    if (noalloc && p.bytes > kda::split_scratch_bytes()) {
+        snprintf(g_last_error, sizeof(g_last_error),
+                 "%s: this split needs %zu bytes of scratch; the library holds %zu (use fewer segments, or the "
+                 "entry point that takes a workspace)", name, p.bytes, kda::split_scratch_bytes());
+        return KDA_ERR_VALUE;
+    }
+    if (!noalloc && workspace_bytes < p.bytes) return KDA_ERR_VALUE;
     kda_status st = check_device();
     if (st != KDA_OK) return st;
+    if (noalloc) {
+        hipError_t e = kda::split_scratch(&workspace);
+        if (e != hipSuccess) {
+            set_error(name, e);
+            return KDA_ERR_HIP;
+        }
+    }
     kda::PrefillArgs a{q, k, v, decay, beta, init_state, nullptr, 1, total_T, H, d_k, d_v,
                        dtype == KDA_BF16, o, final_state, reinterpret_cast<hipStream_t>(stream), gated, a_log};
     unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -337,6 +352,14 @@ kda_status kda_chunk_prefill_split(const void* q, const void* k, const void* v,
                                    void* o, float* final_state, void* stream) {
     return split_impl("kda_chunk_prefill_split launch", q, k, v, log_alpha, beta, nullptr, false, init_state,
                       total_T, H, d_k, d_v, dtype, segments, workspace, workspace_bytes, o, final_state, stream);
+}
+
+kda_status kda_chunk_prefill_split_noalloc(const void* q, const void* k, const void* v,
+                                           const float* log_alpha, const float* beta, const float* init_state,
+                                           int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                           int32_t segments, void* o, float* final_state, void* stream) {
+    return split_impl("kda_chunk_prefill_split_noalloc", q, k, v, log_alpha, beta, nullptr, false, init_state,
+                      total_T, H, d_k, d_v, dtype, segments, nullptr, 0, o, final_state, stream, true);
 }
 
 kda_status kda_chunk_prefill_gated_split(const void* q, const void* k, const void* v,

@@ -117,6 +117,10 @@ hipError_t launch_prefill(const PrefillArgs& a);
 bool prefill_grid_fits(int64_t units, int32_t d_v);
 bool split_grid_fits(int64_t run_units, int64_t trans_units, int32_t d_k, int32_t d_v);
 bool split_correct_grid_fits(int32_t H, int32_t segments, int64_t seg_len);
+// The library's own split scratch on the current device (allocation-free entry
+// point): its address (looked up once per device) and its size.
+hipError_t split_scratch(void** ptr);
+size_t split_scratch_bytes();
 // Bounded in-kernel waits that ran out (a guard against a logic error: each
 // wait's flag is written by a wave that does not wait itself), counted on the
 // current device since the last reset.

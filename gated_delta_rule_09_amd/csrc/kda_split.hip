@@ -24,6 +24,10 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <mutex>
+
+#include "../../include/kda.h"
+
 namespace kda {
 namespace {
 
@@ -284,6 +288,38 @@ hipError_t correct_t(const PrefillArgs& a, const SplitWork& w) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free split entry point: the segment end states,
+// transitions and Phi_t^T q_t rows of one call, in device memory that the code
+// object holds (each device that loads the library holds its own copy until the
+// process ends).  Host code never uses the array's name as an address: the
+// device address is looked up once per device with hipGetSymbolAddress.
+constexpr size_t kSplitScratchBytes = KDA_SPLIT_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kSplitScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+size_t split_scratch_bytes() { return kSplitScratchBytes; }
+
+hipError_t split_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));    // with this device current
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool split_correct_grid_fits(int32_t H, int32_t segments, int64_t seg_len) {
     return grid_fits((int64_t)H * (segments - 1) * ((seg_len + kCorrTok - 1) / kCorrTok), kCorrThreads);

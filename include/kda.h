@@ -238,6 +238,30 @@ kda_status kda_chunk_prefill_split(const void* q, const void* k, const void* v,
                                    void* o, float* final_state, void* stream);
 
 /* The same from decay / write-strength logits (see the gated calls above). */
+/*
+ * kda_chunk_prefill_split_noalloc -- kda_chunk_prefill_split without a
+ * caller-owned workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).
+ *
+ * Same arguments, results and errors as kda_chunk_prefill_split, except that
+ * the workspace is scratch the library holds in its code object:
+ * KDA_SPLIT_SCRATCH_BYTES (64 MiB) on each device the library runs on, kept
+ * until the process ends.  The call itself allocates nothing (no hipMalloc or
+ * allocating library routine).  A split whose kda_split_workspace_bytes exceeds
+ * KDA_SPLIT_SCRATCH_BYTES returns KDA_ERR_VALUE (with kda_last_error naming both
+ * sizes) before any HIP call; fewer segments need less.  No byte of the scratch
+ * has to start at zero: every byte a call reads was written by the same call.
+ * Every call on one device shares that device's scratch: calls that overlap on
+ * one device (other streams, other threads) race and must be ordered by the
+ * caller.
+ */
+#define KDA_SPLIT_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_chunk_prefill_split_noalloc(const void* q, const void* k, const void* v,
+                                           const float* log_alpha, const float* beta, const float* init_state,
+                                           int64_t total_T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                           int32_t segments, void* o, float* final_state, void* stream);
+
 kda_status kda_chunk_prefill_gated_split(const void* q, const void* k, const void* v,
                                          const void* g_logits, const float* a_log, const float* beta_logits,
                                          const float* init_state, int64_t total_T, int32_t H,

@@ -408,3 +408,35 @@ def test_wait_giveups_host_path():
         assert st == 0
     else:
         assert st == 5 and n.value == 7
+
+
+def prefill_split_noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, b=P, init=None, T=4096, H=2, dk=64, dv=64, dt=L.KDA_BF16, seg=4, o=P, fin=P)
+    a.update(kw)
+    return lib.kda_chunk_prefill_split_noalloc(a["q"], a["k"], a["v"], a["la"], a["b"], a["init"], a["T"], a["H"],
+                                               a["dk"], a["dv"], a["dt"], a["seg"], a["o"], a["fin"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), 3), (dict(seg=0), 7), (dict(dk=96), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(q=None), 1),
+    (dict(o=None), 1), (dict(la=MIS), 4), (dict(init=MIS), 4),
+    # a plan beyond the library's scratch: 65,536 tokens x 12 heads x d 128 in 8 segments needs ~200 MB
+    (dict(T=65536, H=12, dk=128, dv=128, seg=8), 7),
+])
+def test_noalloc_split_rejects_bad_arguments_before_touching_the_device(kw, code):
+    assert prefill_split_noalloc(L.load(), **kw) == code
+
+
+def test_noalloc_split_scratch_limit():
+    """The largest plan the scratch holds passes validation; one byte more does not."""
+    lib = L.load()
+    assert L.SPLIT_SCRATCH_BYTES == 64 << 20
+    # 16,384 tokens in 4 segments, 12 heads, d = 128, bf16: end states 3 MB, transitions 2.4 MB and
+    # Phi^T q rows of 12,288 tokens 37.7 MB, under 64 MiB
+    need = lib.kda_split_workspace_bytes(16384, 12, 128, 128, L.KDA_BF16, 4)
+    assert 0 < need <= L.SPLIT_SCRATCH_BYTES
+    assert prefill_split_noalloc(lib, T=16384, H=12, dk=128, dv=128, seg=4) in OK_OR_NO_DEVICE
+    # twice the heads is beyond it
+    assert lib.kda_split_workspace_bytes(16384, 24, 128, 128, L.KDA_BF16, 4) > L.SPLIT_SCRATCH_BYTES
+    assert prefill_split_noalloc(lib, T=16384, H=24, dk=128, dv=128, seg=4) == 7
+    assert b"scratch" in lib.kda_last_error()
