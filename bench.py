@@ -168,7 +168,7 @@ def cpu_baselines():
 
     def pool_run(name, x, heads=None, workers=None):
         r = oracle_pool.prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state, x.cu_seqlens, heads=heads,
-                                workers=workers)
+                                workers=workers, progress=lambda m: print(m, file=sys.stderr, flush=True))
         out[name] = {"seconds": round(r["seconds"], 3), "token_heads": r["token_heads"], "processes": r["workers"],
                      "token_heads_per_s": round(r["token_heads"] / r["seconds"], 1)}
         print(f"[cpu-baselines] {name}: {out[name]}", file=sys.stderr, flush=True)
@@ -200,8 +200,15 @@ def cpu_baselines():
         for p in procs:
             p.stdin.write("go\n")
             p.stdin.flush()
-        res = [json.loads(p.communicate(timeout=1200)[0].strip().splitlines()[-1]) for p in procs]
+        last = t0
+        while any(p.poll() is None for p in procs):
+            time.sleep(0.05)
+            if time.perf_counter() - last > 20:
+                last = time.perf_counter()
+                print(f"  oracle decode: {sum(p.poll() is not None for p in procs)}/{len(procs)} processes done "
+                      f"after {last - t0:.0f} s", file=sys.stderr, flush=True)
         wall = time.perf_counter() - t0
+        res = [json.loads(p.communicate()[0].strip().splitlines()[-1]) for p in procs]
     finally:
         for p in procs:
             if p.poll() is None:
