@@ -24,7 +24,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
            4: "KDA_ERR_ALIGN", 5: "KDA_ERR_NO_DEVICE", 6: "KDA_ERR_HIP", 7: "KDA_ERR_VALUE"}
-ABI_VERSION = 5
+ABI_VERSION = 4
 RMS_EPS = 1e-5      # epsilon of the model's RMSNorm
 SPLIT_SCRATCH_BYTES = 64 << 20   # KDA_SPLIT_SCRATCH_BYTES: the no-alloc split's scratch per device
 
@@ -35,8 +35,6 @@ SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
     "kda_wait_giveups": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), _I32, _VP]),
-    "kda_prefill_pair_mode": (_I32, [_I32]),
-    "kda_prefill_pair_launches": (_I64, []),
     "kda_chunk_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           _I32, _I64, _I32, _I32, _I32, ctypes.c_int,
                                           _VP, _VP, _VP]),
@@ -566,16 +564,3 @@ def wait_giveups(reset: bool = True, device=None) -> int:
     if st != KDA_OK:
         raise KDAError("kda_wait_giveups", st)
     return int(n.value)
-
-
-def prefill_pair_mode(mode: int = -1) -> int:
-    """Select the prefill kernel for bf16 prefills with d_k = d_v = 128: 1 runs
-    the producer/state pair of workgroups wherever its grid fits the device at
-    once (the default), 0 always runs the single-workgroup kernel; any other
-    value only queries.  Returns the previous mode."""
-    return int(load().kda_prefill_pair_mode(int(mode)))
-
-
-def prefill_pair_launches() -> int:
-    """Prefill calls in this process that ran the producer/state pair kernel."""
-    return int(load().kda_prefill_pair_launches())

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_epilogue.hip", "kda_prefill.hip", "kda_prefill_pair.hip", "kda_prologue.hip",
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_epilogue.hip", "kda_prefill.hip", "kda_prologue.hip",
            "kda_split.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -59,10 +59,6 @@ extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
-int32_t kda_prefill_pair_mode(int32_t mode) { return kda::set_prefill_pair_mode(mode); }
-
-int64_t kda_prefill_pair_launches(void) { return kda::prefill_pair_launches(); }
-
 const char* kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "ok";
@@ -84,10 +80,7 @@ kda_status kda_wait_giveups(uint32_t* count, int32_t reset, void* stream) {
     kda_status st = check_device();
     if (st != KDA_OK) return st;
     hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
-    uint32_t pair = 0;
     if (e == hipSuccess) e = kda::read_wait_giveups(count, reset != 0);
-    if (e == hipSuccess) e = kda::read_pair_wait_giveups(&pair, reset != 0);
-    if (e == hipSuccess) *count += pair;
     if (e != hipSuccess) {
         set_error("kda_wait_giveups", e);
         return KDA_ERR_HIP;
@@ -157,9 +150,7 @@ kda_status prefill_impl(const char* name, const void* q, const void* k, const vo
     if (st != KDA_OK) return st;
     kda::PrefillArgs a{q, k, v, decay, beta, init_state, cu_seqlens, N, total_T, H, d_k, d_v,
                        dtype == KDA_BF16, o, final_state, reinterpret_cast<hipStream_t>(stream), gated, a_log};
-    bool used = false;
-    hipError_t e = kda::launch_prefill_pair(a, &used);
-    if (e == hipSuccess && !used) e = kda::launch_prefill(a);
+    hipError_t e = kda::launch_prefill(a);
     if (e != hipSuccess) {
         set_error(name, e);
         return KDA_ERR_HIP;

@@ -111,15 +111,6 @@ bool prologue_grid_fits(int64_t N, int64_t total_T, int32_t H, int32_t d_k, int3
 hipError_t launch_epilogue(const EpilogueArgs& a);
 int64_t epilogue_max_rows(bool bf16, int32_t d_v);
 hipError_t launch_prefill(const PrefillArgs& a);
-// The producer/state pair kernel (bf16, d_k = d_v = 128), launched when every
-// workgroup of its grid can be resident at once and the stream is not being
-// captured; *used tells whether it ran (otherwise the caller runs
-// launch_prefill).  Its ring workspace is allocated on the first use per
-// (device, stream) and kept.
-hipError_t launch_prefill_pair(const PrefillArgs& a, bool* used);
-int set_prefill_pair_mode(int mode);    // 1: where it fits (default), 0: never; returns the old mode
-int64_t prefill_pair_launches();        // pair launches so far in this process
-hipError_t read_pair_wait_giveups(uint32_t* count, bool reset);
 // Whether a launch over `units` (sequence, head) pairs at d_v value columns
 // fits a dispatch; for the time split, also the transition job of `trans_units`
 // pairs at d_k columns.

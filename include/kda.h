@@ -72,7 +72,7 @@ typedef enum {
 } kda_dtype;
 
 /* Version of this interface; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 4
 int kda_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -84,18 +84,13 @@ const char* kda_last_error(void);
 /*
  * kda_wait_giveups -- count of bounded in-kernel waits that ran out.
  *
- * The single-workgroup prefill kernel's state waves wait on a flag in LDS
- * before reading a triangular inverse that another wave of the workgroup
- * publishes.  Every such flag is written by a wave whose own path to that
- * write has no waits, so the wait always ends; its bound (2^22 polls) only
- * guards against a logic error.  The two workgroups of the pair kernel (see
- * kda_prefill_pair_mode) wait on each other's progress words in device memory;
- * the launch is cooperative, so both are resident and the waits end; their
- * bound (2^20 polls) guards against the same kind of error.  A wait that
- * reaches its bound does not hang the GPU: the wave goes on with whatever the
- * memory holds (a pair workgroup stops waiting altogether) and adds one to a
- * counter in device memory, and the outputs of that launch are then not to be
- * trusted.
+ * The prefill kernel's state waves wait on a flag in LDS before reading a
+ * triangular inverse that another wave of the workgroup publishes.  Every such
+ * flag is written by a wave whose own path to that write has no waits, so the
+ * wait always ends; its bound (2^22 polls) only guards against a logic error.
+ * A wait that reaches the bound does not hang the GPU: the wave goes on with
+ * whatever the LDS holds and adds one to a counter in device memory, and the
+ * outputs of that launch are then not to be trusted.
  *
  *   count  : (host) receives the counter of the current device.
  *   reset  : non-zero sets the counter back to zero after reading it.
@@ -107,34 +102,6 @@ const char* kda_last_error(void);
  * A non-zero count returns KDA_OK and also sets kda_last_error's text.
  */
 kda_status kda_wait_giveups(uint32_t* count, int32_t reset, void* stream);
-
-/*
- * kda_prefill_pair_mode -- choose the prefill kernel of kda_chunk_prefill and
- * kda_chunk_prefill_gated (and of the epilogue variant built on them).
- *
- * bf16 prefills with d_k = d_v = 128 run as a pair of workgroups per
- * (sequence, head) -- one forming each chunk's state-independent operands and
- * inverses, one carrying the state (the chunkwise form of section 1.2 of the
- * notes, split across two CUs) -- whenever the whole grid (16 workgroups per 8
- * pairs) can be resident at once, as at N x H <= 128 on 256 CUs, and the
- * stream is not being captured.  The pair exchanges each chunk through a ring
- * in device memory, which the library allocates on the first such call on a
- * (device, stream) and keeps until the process ends: 3 x 59,392 bytes per
- * pair for half the CU count, about 23 MB on MI355X.  If that allocation fails
- * the call runs the single-workgroup kernel instead.  Every other prefill runs
- * the single-workgroup kernel; both give the same results up to rounding.
- *
- *   mode : 1 uses the pair kernel where it fits (the default), 0 never uses
- *          it; any other value changes nothing.  Process-wide, not
- *          synchronised with calls in flight on other threads.
- *
- * Returns the mode in force before the call.  Needs no device.
- */
-int32_t kda_prefill_pair_mode(int32_t mode);
-
-/* Number of prefill calls in this process that ran the pair kernel (see
- * kda_prefill_pair_mode); for tests and diagnostics.  Needs no device. */
-int64_t kda_prefill_pair_launches(void);
 
 /*
  * kda_chunk_prefill -- KDA over a packed batch of N sequences.

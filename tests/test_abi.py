@@ -32,24 +32,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.kda_abi_version() == L.ABI_VERSION == 5
+    assert lib.kda_abi_version() == L.ABI_VERSION == 4
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
-
-
-def test_prefill_pair_mode_switch_needs_no_device():
-    lib = L.load()
-    old = lib.kda_prefill_pair_mode(-1)
-    assert old in (0, 1)
-    try:
-        assert lib.kda_prefill_pair_mode(0) == old
-        assert lib.kda_prefill_pair_mode(7) == 0          # not a mode: nothing changes
-        assert lib.kda_prefill_pair_mode(1) == 0
-        assert lib.kda_prefill_pair_mode(-1) == 1
-    finally:
-        lib.kda_prefill_pair_mode(old)
-    assert lib.kda_prefill_pair_launches() >= 0
 
 
 # Fake, aligned, never-dereferenced addresses: validation fails before any HIP call.
