@@ -341,7 +341,7 @@ __device__ __forceinline__ float lane_elem(const uint32_t (&w)[N], int cc) {
 // operands with d_k = 128 do not fit twice in 160 KB: they get one buffer, and
 // the two roles then take turns on it instead of overlapping.
 // ---------------------------------------------------------------------------
-template <typename OT, int DK>
+template <typename OT, int DK, bool GATED>
 struct Plan {
     static constexpr int NBUF = (sizeof(OT) == 4 && DK == 128) ? 1 : 2;
     static constexpr int ES = sizeof(OT);
@@ -368,12 +368,21 @@ struct Plan {
     static constexpr int MSTR = 20;                                // fp32 stride of M^T rows (16-byte aligned)
     static constexpr int MS = DEC + kTiles * DK * 4;               // [4][16][MSTR] fp32 M^T per tile
     static constexpr int BS = MS + kTiles * 16 * MSTR * 4;         // [4][16] fp32 beta per tile
-    static constexpr int BUF = BS + kTiles * 16 * 4;
-    // scratch
-    static constexpr int KB = NBUF * BUF;                          // [C][LDK]   k * 2^{-x}
-    static constexpr int FLAG = KB + kC * LDK * ES;                // [4] int: chunk whose A of tile i is ready
+    // Gated bf16: the key Gram M of a tile is formed by the state wave that
+    // inverts it, one chunk after the producer wave wrote the column operand,
+    // so that operand is kept per buffer.  The gated producer waves also map
+    // every decay logit (a sigmoid each), and moving M off them measured 3-4%
+    // faster at 64K x 96; with plain log-decay inputs it measured 3% slower,
+    // and fp32 has no room for a second copy, so there the producer waves
+    // form M.
+    static constexpr bool GSD = ES == 2 && GATED;
+    static constexpr int KBIN = BS + kTiles * 16 * 4;              // [C][LDK]   k * 2^{-x} (GSD)
+    static constexpr int BUF = GSD ? KBIN + kC * LDK * ES : KBIN;
+    // scratch (producer waves only)
+    static constexpr int KB = NBUF * BUF;                          // [C][LDK]   k * 2^{-x} (not GSD)
+    static constexpr int FLAG = GSD ? KB : KB + kC * LDK * ES;     // [4] int: chunk whose A of tile i is ready
     static constexpr int TOTAL = FLAG + 16;
-    static_assert(BUF % 16 == 0 && KB % 16 == 0, "alignment");
+    static_assert(BUF % 16 == 0 && KB % 16 == 0 && KBIN % 16 == 0, "alignment");
     static_assert(TOTAL <= 160 * 1024, "LDS plan exceeds 160 KB");
 };
 
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     const int units = J.units;
     using OT = T;
     using OP = Op<OT>;
-    using PL = Plan<OT, DK>;
+    using PL = Plan<OT, DK, GATED>;
     using Xop = typename OP::Xop;
     constexpr int KS = OP::KS;
     constexpr int CPL = 8;                // SI: key channels per lane (16-byte loads of bf16 q, k)
@@ -547,6 +556,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         float* sDEC = reinterpret_cast<float*>(buf + PL::DEC);
         float* sMS = reinterpret_cast<float*>(buf + PL::MS);
         float* sBS = reinterpret_cast<float*>(buf + PL::BS);
+        OT* sKBc = PL::GSD ? reinterpret_cast<OT*>(buf + PL::KBIN) : sKB;
         const int ti = wave;
         // Lane = (key channels cb .. cb+7; tile positions pb .. pb+RP-1).
         // alpha = 2^{l2}; e1 = prefix products over the tile, e2 = suffix
@@ -646,7 +656,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             OP::put8(sQE1 + orow, qe1[0], qe1[1]);
             OP::put8(sKE1 + orow, ke1[0], ke1[1]);
             OP::put8(sKE2 + (pb + r) * PL::LDK2 + cb, ke2[0], ke2[1]);
-            OP::put8(sKB + orow, kb[0], kb[1]);
+            OP::put8(sKBc + orow, kb[0], kb[1]);
             // Row r of q and k is consumed: load the same row of the next chunk.
             load_qk_row(rq_next, r);
             __builtin_amdgcn_sched_barrier(0);
@@ -662,17 +672,18 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         wave_lds_sync();
 
         // P and M of the tile, transposed (D[s][r] = sum_c Kb[s][c] X[r][c]):
-        // lane holds row r = l16, columns s = 4 lg + e.
+        // lane holds row r = l16, columns s = 4 lg + e.  (bf16: M is formed by
+        // the state wave that inverts the tile.)
         {
             const OT* rq = sQE1 + 16 * ti * PL::LDK;
             const OT* rk = sKE1 + 16 * ti * PL::LDK;
-            const OT* rb = sKB + 16 * ti * PL::LDK;
+            const OT* rb = sKBc + 16 * ti * PL::LDK;
             f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const typename OP::Frag fb = OP::frag(rb, PL::LDK, ks * KS);
                 accP = OP::mma(fb, OP::frag(rq, PL::LDK, ks * KS), accP);
-                accM = OP::mma(fb, OP::frag(rk, PL::LDK, ks * KS), accM);
+                if constexpr (!PL::GSD) accM = OP::mma(fb, OP::frag(rk, PL::LDK, ks * KS), accM);
             }
             f32x4 vp;
 #pragma unroll
@@ -680,7 +691,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
                 const int s = 4 * lg + e;
                 vp[e] = s <= l16 ? accP[e] : 0.f;
                 // M^T[s][r], columns in (r % 4, r / 4) order
-                sMS[(ti * 16 + s) * PL::MSTR + 4 * (l16 & 3) + (l16 >> 2)] = s < l16 ? accM[e] : 0.f;
+                if constexpr (!PL::GSD)
+                    sMS[(ti * 16 + s) * PL::MSTR + 4 * (l16 & 3) + (l16 >> 2)] = s < l16 ? accM[e] : 0.f;
             }
             OP::put4(sPD + (ti * 16 + l16) * PL::LD16 + 4 * lg, vp);
         }
@@ -691,8 +703,23 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
     auto inverse = [&](int64_t c, int ti) {
         unsigned char* buf = smem + (c % PL::NBUF) * PL::BUF;
         OT* sAD = reinterpret_cast<OT*>(buf + PL::AD);
-        const float* sMS = reinterpret_cast<const float*>(buf + PL::MS);
+        float* sMS = reinterpret_cast<float*>(buf + PL::MS);
         const float* sBS = reinterpret_cast<const float*>(buf + PL::BS);
+        if constexpr (PL::GSD) {
+            // M of the tile (transposed, as the producer waves would store it).
+            const OT* rk = reinterpret_cast<const OT*>(buf + PL::KE1) + 16 * ti * PL::LDK;
+            const OT* rb = reinterpret_cast<const OT*>(buf + PL::KBIN) + 16 * ti * PL::LDK;
+            f32x4 accM = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                accM = OP::mma(OP::frag(rb, PL::LDK, ks * KS), OP::frag(rk, PL::LDK, ks * KS), accM);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 4 * lg + e;
+                sMS[(ti * 16 + s) * PL::MSTR + 4 * (l16 & 3) + (l16 >> 2)] = s < l16 ? accM[e] : 0.f;
+            }
+            wave_lds_sync();
+        }
         // A = (I + Diag(b) M)^{-1} Diag(b) by right-looking substitution on
         // all 64 lanes: lane = (column j = lane / 4, row residue q = lane % 4)
         // and holds rows r = 4 m + q, m = 0..3, of column j of X = (I +
@@ -913,7 +940,7 @@ int64_t job_blocks(int64_t units) {
 // One launch of the jobs j0 and j1 (j1.units may be 0).
 template <typename T, int DK, int DV, bool GATED>
 hipError_t launch_jobs(const PrefillArgs& a, PrefillJob j0, PrefillJob j1) {
-    using PL = Plan<T, DK>;
+    using PL = Plan<T, DK, GATED>;
     auto kern = prefill_kernel<T, DK, DV, GATED>;
     // The dynamic-LDS limit is set on every launch: it is a host-side property of
     // the function on the current device, cheap to set, and no cached flag can
