@@ -674,7 +674,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         // P and M of the tile, transposed (D[s][r] = sum_c Kb[s][c] X[r][c]):
         // lane holds row r = l16, columns s = 4 lg + e.  (bf16: M is formed by
         // the state wave that inverts the tile.)
-        {
+        if constexpr (!PL::GSD) {
             const OT* rq = sQE1 + 16 * ti * PL::LDK;
             const OT* rk = sKE1 + 16 * ti * PL::LDK;
             const OT* rb = sKBc + 16 * ti * PL::LDK;
@@ -706,18 +706,27 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         float* sMS = reinterpret_cast<float*>(buf + PL::MS);
         const float* sBS = reinterpret_cast<const float*>(buf + PL::BS);
         if constexpr (PL::GSD) {
-            // M of the tile (transposed, as the producer waves would store it).
+            // P and M of the tile (transposed, as the producer waves would store
+            // them); P is published with A (it is written before A's flag).
+            const OT* rq = reinterpret_cast<const OT*>(buf + PL::QE1) + 16 * ti * PL::LDK;
             const OT* rk = reinterpret_cast<const OT*>(buf + PL::KE1) + 16 * ti * PL::LDK;
             const OT* rb = reinterpret_cast<const OT*>(buf + PL::KBIN) + 16 * ti * PL::LDK;
-            f32x4 accM = {0.f, 0.f, 0.f, 0.f};
+            OT* sPD = reinterpret_cast<OT*>(buf + PL::PD);
+            f32x4 accP = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                accM = OP::mma(OP::frag(rb, PL::LDK, ks * KS), OP::frag(rk, PL::LDK, ks * KS), accM);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const typename OP::Frag fb = OP::frag(rb, PL::LDK, ks * KS);
+                accP = OP::mma(fb, OP::frag(rq, PL::LDK, ks * KS), accP);
+                accM = OP::mma(fb, OP::frag(rk, PL::LDK, ks * KS), accM);
+            }
+            f32x4 vp;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = 4 * lg + e;
+                vp[e] = s <= l16 ? accP[e] : 0.f;
                 sMS[(ti * 16 + s) * PL::MSTR + 4 * (l16 & 3) + (l16 >> 2)] = s < l16 ? accM[e] : 0.f;
             }
+            OP::put4(sPD + (ti * 16 + l16) * PL::LD16 + 4 * lg, vp);
             wave_lds_sync();
         }
         // A = (I + Diag(b) M)^{-1} Diag(b) by right-looking substitution on
@@ -804,7 +813,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             for (int ct = 0; ct < NCT; ++ct) t.kseg[ct] = OP::seg(krow + 16 * ct);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) t.qseg[ct] = OP::seg(qrow + 16 * ct);
-            t.pseg = OP::seg(sPD + (16 * i + l16) * PL::LD16);
+            if constexpr (!PL::GSD) t.pseg = OP::seg(sPD + (16 * i + l16) * PL::LD16);   // (GSD: after A's flag)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) t.eseg[ct] = OP::seg_t(sKE2 + 16 * i * PL::LDK2 + 16 * ct, tro, PL::LDK2);
             const float* dp = sDEC + i * DK + 16 * ((VPL * l16) >> 2) + 4 * lg + ((VPL * l16) & 3);
@@ -823,6 +832,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
         for (int i = 0; i < kTiles; ++i) {
             if (i != wave - kSIW) wait_a(c, i);
             const Seg aseg = OP::seg(sAD + (16 * i + l16) * PL::LD16);
+            Seg pseg_f{};
+            if constexpr (PL::GSD) pseg_f = OP::seg(sPD + (16 * i + l16) * PL::LD16);   // P is published with A
             if constexpr (NOPS == 2) {
                 if (i + 1 < kTiles) load_ops(i + 1, ops[(i + 1) & 1]);
             } else {
@@ -832,7 +843,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void prefill_kernel(
             const auto& kseg = cur.kseg;
             const auto& qseg = cur.qseg;
             const auto& eseg = cur.eseg;
-            const Seg pseg = cur.pseg;
+            const Seg pseg = PL::GSD ? pseg_f : cur.pseg;
             const auto& decv = cur.decv;
             Xop Sop[NCT];
 #pragma unroll
