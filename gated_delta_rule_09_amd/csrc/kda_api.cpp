@@ -204,11 +204,10 @@ kda_status split_impl(const char* name, const void* q, const void* k, const void
         return prefill_impl(name, q, k, v, decay, beta, a_log, gated, init_state, nullptr, 1, total_T, H, d_k, d_v,
                             dtype, o, final_state, stream);
     if (!kda::split_grid_fits((int64_t)p.segments * H, (int64_t)(p.segments - 1) * H, d_k, d_v)) return KDA_ERR_SHAPE;
-    // The correction addresses 512 tokens of a head with 32-bit byte offsets,
-    // and its grid has one workgroup per (head, 512 tokens of a segment).
+    // The correction addresses the tokens of a head in pieces of at least 512
+    // (its grid is two workgroups per CU) with 32-bit byte offsets.
     const int64_t es = dtype == KDA_BF16 ? 2 : 4;
     if (512 * (int64_t)H * (d_k > d_v ? d_k : d_v) * es > (int64_t)UINT32_MAX) return KDA_ERR_SHAPE;
-    if (!kda::split_correct_grid_fits(H, p.segments, p.seg_len)) return KDA_ERR_SHAPE;
     if (!q || !k || !v || !decay || !beta || !o || (gated && !a_log) || (!noalloc && !workspace)) return KDA_ERR_NULL;
     const void* ptrs[] = {q, k, v, decay, beta, a_log, init_state, o, final_state, noalloc ? nullptr : workspace};
     for (const void* ptr : ptrs)

@@ -116,7 +116,6 @@ hipError_t launch_prefill(const PrefillArgs& a);
 // pairs at d_k columns.
 bool prefill_grid_fits(int64_t units, int32_t d_v);
 bool split_grid_fits(int64_t run_units, int64_t trans_units, int32_t d_k, int32_t d_v);
-bool split_correct_grid_fits(int32_t H, int32_t segments, int64_t seg_len);
 // The library's own split scratch on the current device (allocation-free entry
 // point): its address (looked up once per device) and its size.
 hipError_t split_scratch(void** ptr);

@@ -107,19 +107,23 @@ __global__ __launch_bounds__(256) void split_scan_kernel(float* __restrict__ end
 }
 
 // ---------------------------------------------------------------------------
-// Correction.  One workgroup (8 waves) per (head, segment p >= 1, block of up
-// to 512 tokens of that segment); a wave takes 16 tokens of each 128-token
-// sub-block.  The state that segment p starts from, S = ends[p - 1], is staged
-// transposed in LDS (ST[j][m] = S[m][j]): a thread takes one column j and 8 (or
-// 4) consecutive rows m, so the global reads are coalesced over j and each
-// LDS write is one 16-byte row piece (conflict-free at that width).  The
+// Correction.  The tokens of segments p >= 1 of every head, in (segment, head,
+// token) order, are cut into one contiguous range per workgroup (8 waves), and
+// the grid holds two workgroups per CU, so that the device is filled once and
+// no partial last round is left.  A range is walked in pieces, one per
+// (segment, head) it crosses; a wave takes 16 tokens of each 128-token
+// sub-block of a piece.  The state that segment p starts from, S = ends[p - 1],
+// is staged transposed in LDS (ST[j][m] = S[m][j]) once per (segment, head): a
+// thread takes one column j and 8 (or 4) consecutive rows m, so the global
+// reads are coalesced over j and each LDS write is one 16-byte row piece
+// (conflict-free at that width).  The
 // product is formed as D = ST * QT^T, so a lane (n = l % 16, g = l / 16) ends
 // with the correction of token n for the four consecutive value columns
 // 16 ct + 4 g + e, which is also the layout of its 8- or 16-byte read-modify-
 // write of o.  The o words are loaded beside the qt operands, before the
 // products, so both loads are in flight together.
 // ---------------------------------------------------------------------------
-constexpr int kCorrTok = 512;
+constexpr int kCorrTok = 128;        // tokens of one sub-block (8 waves x 16)
 constexpr int kCorrThreads = 512;
 
 template <typename T, int DK, int DV> struct CorrOps;
@@ -220,48 +224,66 @@ template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kCorrThreads) void split_correct_kernel(const float* __restrict__ ends,
                                                                      const T* __restrict__ qt, T* __restrict__ o,
                                                                      int64_t total_T, int H, int64_t seg_len,
-                                                                     int blocks_per_seg, int segments) {
+                                                                     int segments, int64_t per_wg, int64_t piece_cap) {
     using CO = CorrOps<T, DK, DV>;
     static_assert(kCorrThreads % DV == 0, "staging");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];   // CO::LDS_BYTES
-    int b = blockIdx.x;
-    const int h = b % H;
-    b /= H;
-    const int p = 1 + b / blocks_per_seg;                   // segment
-    const int64_t blk = b % blocks_per_seg;
-    const int64_t seg_end = ((int64_t)p + 1) * seg_len < total_T ? ((int64_t)p + 1) * seg_len : total_T;
-    const int64_t t_begin = (int64_t)p * seg_len + blk * kCorrTok;
-    if (p >= segments || t_begin >= seg_end) return;
-    const int64_t t_end = t_begin + kCorrTok < seg_end ? t_begin + kCorrTok : seg_end;
-
+    // Segments 1 .. P - 2 hold seg_len tokens each, the last one last_len.
+    const int64_t last_len = total_T - (int64_t)(segments - 1) * seg_len;
+    const int64_t full = (int64_t)(segments - 2) * H * seg_len;
+    const int64_t total = full + (int64_t)H * last_len;
+    int64_t f = (int64_t)blockIdx.x * per_wg;
+    const int64_t f_end = f + per_wg < total ? f + per_wg : total;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i = lane & 15, g = lane >> 4;
-    CO::stage(smem, ends + ((size_t)(p - 1) * H + h) * DK * DV, tid);
-    __syncthreads();
-
-    // Row ranges: tokens t_begin .. t_end - 1 of this head.  Rows past t_end
-    // read as zero and their stores are dropped.
-    const uint32_t rows = (uint32_t)(t_end - t_begin - 1) * (uint32_t)H + 1u;
-    const Rsrc rq = make_rsrc(qt + ((t_begin - seg_len) * H + h) * DK, rows * DK * (uint32_t)sizeof(T));
-    const Rsrc ro = make_rsrc(o + (t_begin * H + h) * DV, rows * DV * (uint32_t)sizeof(T));
-    for (int64_t t0 = 0; t0 < t_end - t_begin; t0 += 16 * (kCorrThreads / 64)) {
-        const uint32_t tok = (uint32_t)(t0 + 16 * wave + i);   // this lane's token (operand row)
-        const uint32_t orow = tok * (uint32_t)H * DV;
-        typename CO::QW qw;
-        CO::load_q(qw, rq, tok * (uint32_t)H * DK * (uint32_t)sizeof(T));
-        typename CO::OW ow[DV / 16];
+    int64_t staged = -1;                     // (segment - 1) * H + head of the staged state
+    while (f < f_end) {
+        int64_t pair, t_in, len;
+        if (f < full) {
+            pair = f / seg_len;
+            t_in = f - pair * seg_len;
+            len = seg_len;
+        } else {
+            const int64_t r = (f - full) / last_len;
+            pair = (int64_t)(segments - 2) * H + r;
+            t_in = f - full - r * last_len;
+            len = last_len;
+        }
+        const int p = 1 + (int)(pair / H), h = (int)(pair % H);
+        int64_t n = len - t_in < f_end - f ? len - t_in : f_end - f;
+        n = n < piece_cap ? n : piece_cap;
+        if (pair != staged) {
+            __syncthreads();                 // the previous piece is done with the staged state
+            CO::stage(smem, ends + ((size_t)(p - 1) * H + h) * DK * DV, tid);
+            __syncthreads();
+            staged = pair;
+        }
+        const int64_t t_begin = (int64_t)p * seg_len + t_in, t_end = t_begin + n;
+        // Row ranges: tokens t_begin .. t_end - 1 of this head.  Rows past t_end
+        // read as zero and their stores are dropped.
+        const uint32_t rows = (uint32_t)(t_end - t_begin - 1) * (uint32_t)H + 1u;
+        const Rsrc rq = make_rsrc(qt + ((t_begin - seg_len) * H + h) * DK, rows * DK * (uint32_t)sizeof(T));
+        const Rsrc ro = make_rsrc(o + (t_begin * H + h) * DV, rows * DV * (uint32_t)sizeof(T));
+        for (int64_t t0 = 0; t0 < n; t0 += 16 * (kCorrThreads / 64)) {
+            const uint32_t tok = (uint32_t)(t0 + 16 * wave + i);   // this lane's token (operand row)
+            const uint32_t orow = tok * (uint32_t)H * DV;
+            typename CO::QW qw;
+            CO::load_q(qw, rq, tok * (uint32_t)H * DK * (uint32_t)sizeof(T));
+            typename CO::OW ow[DV / 16];
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct) ow[ct] = CO::load_o(ro, (orow + 16 * ct + 4 * g) * (uint32_t)sizeof(T));
-        // The staged operands are read again for every sub-block rather than
-        // held in registers, which keeps room for more waves per SIMD.
-        __asm__ volatile("" ::: "memory");
-        f32x4 acc[DV / 16];
+            for (int ct = 0; ct < DV / 16; ++ct) ow[ct] = CO::load_o(ro, (orow + 16 * ct + 4 * g) * (uint32_t)sizeof(T));
+            // The staged operands are read again for every sub-block rather than
+            // held in registers, which keeps room for more waves per SIMD.
+            __asm__ volatile("" ::: "memory");
+            f32x4 acc[DV / 16];
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        CO::product(smem, qw, acc);
+            for (int ct = 0; ct < DV / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            CO::product(smem, qw, acc);
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct)
-            CO::store_o(ro, (orow + 16 * ct + 4 * g) * (uint32_t)sizeof(T), ow[ct], acc[ct]);
+            for (int ct = 0; ct < DV / 16; ++ct)
+                CO::store_o(ro, (orow + 16 * ct + 4 * g) * (uint32_t)sizeof(T), ow[ct], acc[ct]);
+        }
+        f += n;
     }
 }
 
@@ -273,17 +295,32 @@ hipError_t scan_t(const PrefillArgs& a, const SplitWork& w) {
     return hipGetLastError();
 }
 
+// Workgroups of the correction: two per CU (their LDS fits twice), each with
+// a whole number of 128-token sub-blocks, unless there are fewer.
 template <typename T, int DK, int DV>
 hipError_t correct_t(const PrefillArgs& a, const SplitWork& w) {
-    const int64_t bps = (w.seg_len + kCorrTok - 1) / kCorrTok;
-    const int64_t blocks = (int64_t)a.H * (w.segments - 1) * bps;
-    if (blocks <= 0) return hipSuccess;
+    const int64_t last_len = a.total_T - (int64_t)(w.segments - 1) * w.seg_len;
+    const int64_t total = (int64_t)(w.segments - 2) * a.H * w.seg_len + (int64_t)a.H * last_len;
+    if (w.segments < 2 || total <= 0) return hipSuccess;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int64_t units = (total + kCorrTok - 1) / kCorrTok;              // 128-token sub-blocks
+    const int64_t want = 2 * (int64_t)(cus > 0 ? cus : 1);
+    const int64_t per_wg = kCorrTok * ((units + want - 1) / want);
+    const int64_t blocks = (total + per_wg - 1) / per_wg;
+    // Pieces short enough for the 32-bit buffer offsets of one (segment, head):
+    // at least 512 tokens, since the host checks 512 H max(d_k, d_v) bytes < 2^32.
+    const int64_t row_bytes = (int64_t)a.H * (DK > DV ? DK : DV) * (int64_t)sizeof(T);
+    const int64_t piece_cap = kCorrTok * ((((int64_t)1 << 31) / row_bytes) / kCorrTok);
+    if (piece_cap < kCorrTok) return hipErrorInvalidValue;
     auto kern = split_correct_kernel<T, DK, DV>;
     constexpr int lds = CorrOps<T, DK, DV>::LDS_BYTES;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kCorrThreads), lds, a.stream,
-                       w.ends, (const T*)w.qt, (T*)a.o, a.total_T, a.H, w.seg_len, (int)bps, w.segments);
+                       w.ends, (const T*)w.qt, (T*)a.o, a.total_T, a.H, w.seg_len, w.segments, per_wg, piece_cap);
     return hipGetLastError();
 }
 
@@ -319,10 +356,6 @@ hipError_t split_scratch(void** ptr) {
     }
     *ptr = g_scratch_ptr[dev];
     return hipSuccess;
-}
-
-bool split_correct_grid_fits(int32_t H, int32_t segments, int64_t seg_len) {
-    return grid_fits((int64_t)H * (segments - 1) * ((seg_len + kCorrTok - 1) / kCorrTok), kCorrThreads);
 }
 
 hipError_t launch_split_scan(const PrefillArgs& a, const SplitWork& w) {
