@@ -368,13 +368,13 @@ struct Plan {
     static constexpr int MSTR = 20;                                // fp32 stride of M^T rows (16-byte aligned)
     static constexpr int MS = DEC + kTiles * DK * 4;               // [4][16][MSTR] fp32 M^T per tile
     static constexpr int BS = MS + kTiles * 16 * MSTR * 4;         // [4][16] fp32 beta per tile
-    // Gated bf16: the key Gram M of a tile is formed by the state wave that
-    // inverts it, one chunk after the producer wave wrote the column operand,
-    // so that operand is kept per buffer.  The gated producer waves also map
-    // every decay logit (a sigmoid each), and moving M off them measured 3-4%
-    // faster at 64K x 96; with plain log-decay inputs it measured 3% slower,
-    // and fp32 has no room for a second copy, so there the producer waves
-    // form M.
+    // Gated bf16: both Gram products of a tile (P and M) are formed by the
+    // state wave that inverts it, one chunk after the producer wave wrote the
+    // column operand, so that operand is kept per buffer.  The gated producer
+    // waves also map every decay logit (a sigmoid each), and moving the Grams
+    // off them measured 5-8% faster at 64K x 96; with plain log-decay inputs
+    // it measured 3-7% slower, and fp32 has no room for a second copy, so
+    // there the producer waves form them.
     static constexpr bool GSD = ES == 2 && GATED;
     static constexpr int KBIN = BS + kTiles * 16 * 4;              // [C][LDK]   k * 2^{-x} (GSD)
     static constexpr int BUF = GSD ? KBIN + kC * LDK * ES : KBIN;
