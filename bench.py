@@ -668,6 +668,40 @@ def record_counters(pmc_dir: str, copy_gib: float):
     print(f"wrote {os.path.relpath(path, ROOT)}")
 
 
+def time_stream_reference(dev, stream, gib=3.0, reps=10):
+    """Plain streaming rates of this GPU, as context for the HBM fractions: torch's own in-place scale
+    (read:write 1:1), add (2:1), fill (write only) and copy over fp32 buffers of `gib` GiB each.
+    Median of `reps` launches after one untimed launch."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a).fill_(2.0)
+    c = torch.empty_like(a)
+    nb = 4 * n
+    ops = {"inplace_scale_1to1": (lambda: a.mul_(1.0), 2 * nb),
+           "copy_1to1": (lambda: c.copy_(a), 2 * nb),
+           "add_2to1": (lambda: torch.add(a, b, out=c), 3 * nb),
+           "fill_write_only": (lambda: c.fill_(3.0), nb)}
+    out = {"buffer_gib": gib}
+    for name, (fn, moved) in ops.items():
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        ts.sort()
+        out[name + "_gbps"] = round(moved / (ts[len(ts) // 2] * 1e-3) / 1e9, 1)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -687,6 +721,8 @@ def main():
                          "split at that length with 12 heads")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (counter calibration)")
+    ap.add_argument("--stream-reference", action="store_true",
+                    help="also time torch's plain streaming ops (in-place scale, copy, add, fill) on 3 GiB buffers")
     ap.add_argument("--record-counters", metavar="PMC_DIR",
                     help="no GPU run: build profiles/hbm_traffic.json from the rocprofv3 passes under PMC_DIR "
                          "(fetch/, write/, util/) of a run made with --calibrate-copy-gib")
@@ -818,6 +854,9 @@ def main():
             torch.cuda.empty_cache()
             import gated_delta_rule_09_amd as lib
             res["capacity_split"] = time_split_capacity(args, dev, stream, ki, lib)
+    if args.stream_reference:
+        torch.cuda.empty_cache()
+        res["stream_reference"] = time_stream_reference(dev, stream)
     from gated_delta_rule_09_amd import wait_giveups
     res["wait_giveups"] = wait_giveups()
     if not args.no_cpu_baseline:
