@@ -1,7 +1,8 @@
-"""Fans the fp64 oracle out over child processes, one slice of heads each
-(test infrastructure: the GPU parity tests use it to compare every head of the
-larger workloads, and bench.py's oracle timings use it to time the oracle on
-the host cores).
+"""Fans the fp64 oracle out over child processes, one slice of heads (prefill)
+or of sequences (decode) each (test infrastructure: the GPU parity tests use
+it to compare every head of the larger prefill workloads and every pair of
+the decode workload, and bench.py's oracle timings use it to time the oracle
+on the host cores).
 
 Heads are independent, so each child runs the plain token loop of the oracle
 on its slice and nothing is shared.  Inputs travel as .npy files in a scratch
@@ -131,3 +132,89 @@ def prefill(q, k, v, decay, beta, init_state=None, cu_seqlens=None, a_log=None, 
     if return_o_ref:
         res["o_ref"] = o_ref
     return res
+
+
+class DecodeRun:
+    """The oracle decode over every (sequence, head) pair of a run of steps,
+    split over child processes by sequence.
+
+    Used as a context manager (its scratch directory is removed on exit).
+    The caller saves the state before the first step (save_state0), then each
+    step's inputs and the GPU's output as it goes (save_step), and finally
+    calls compare() with the GPU's state after the last step.  Each child then
+    runs the oracle's decode steps on its sequences in fp64 from the saved
+    state.  compare() returns rel_o (the largest per-step max |gpu - ref| /
+    max |ref| of o), rel_f (the same for the final state), finite, seconds
+    and pair_steps."""
+
+    def __init__(self, N: int, H: int, d_k: int, d_v: int, workers=None):
+        self.N, self.steps = N, 0
+        W = max(1, min(workers or host_cores(), N))
+        self.ranges = [(int(a[0]), int(a[-1]) + 1) for a in np.array_split(np.arange(N), W) if len(a)]
+        per_step = N * H * (8 * d_k + 4 * d_v + 4)      # q, k, v, o in bf16; log alpha and beta fp32
+        self.root = _scratch(100 * per_step + 2 * N * H * d_k * d_v * 4)
+        self.dirs = []
+        for wi in range(len(self.ranges)):
+            d = os.path.join(self.root, f"w{wi}")
+            os.makedirs(d)
+            self.dirs.append(d)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        shutil.rmtree(self.root, ignore_errors=True)
+        return False
+
+    def _split_save(self, name, t):
+        t = t.detach()
+        for d, (a, b) in zip(self.dirs, self.ranges):
+            _save(d, name, t[a:b])
+
+    def save_state0(self, state):
+        self._split_save("state0", state.cpu())
+
+    def save_step(self, x: dict, o):
+        s = self.steps
+        for name, key in (("q", "q"), ("k", "k"), ("v", "v"), ("decay", "log_alpha"), ("beta", "beta")):
+            self._split_save(f"{name}_{s}", x[key].cpu())
+        self._split_save(f"o_gpu_{s}", o.cpu())
+        self.steps += 1
+
+    def compare(self, fin_gpu, progress=None) -> dict:
+        self._split_save("fin_gpu", fin_gpu.cpu())
+        for d in self.dirs:
+            with open(os.path.join(d, "meta.json"), "w") as f:
+                json.dump({"kind": "decode", "steps": self.steps}, f)
+        env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+        t0 = time.perf_counter()
+        procs = [subprocess.Popen([sys.executable, WORKER, d], env=env) for d in self.dirs]
+        try:
+            last = t0
+            while any(p.poll() is None for p in procs):
+                time.sleep(0.05)
+                if progress is not None and time.perf_counter() - last > 20:
+                    last = time.perf_counter()
+                    progress(f"  oracle: {sum(p.poll() is not None for p in procs)}/{len(procs)} processes done "
+                             f"after {last - t0:.0f} s")
+        finally:
+            for p in procs:
+                if p.poll() is None:
+                    p.kill()
+                    p.wait()
+        wall = time.perf_counter() - t0
+        if any(p.returncode != 0 for p in procs):
+            raise RuntimeError(f"oracle workers failed: {[p.returncode for p in procs]}")
+        stats = []
+        for d in self.dirs:
+            with open(os.path.join(d, "stats.json")) as f:
+                stats.append(json.load(f))
+        rel_o = 0.0
+        for s in range(self.steps):
+            den = max(st["o_ref_max"][s] for st in stats)
+            rel_o = max(rel_o, max(st["o_err_max"][s] for st in stats) / (den if den > 0 else 1.0))
+        den = max(st["f_ref_max"] for st in stats)
+        return {"rel_o": rel_o, "rel_f": max(st["f_err_max"] for st in stats) / (den if den > 0 else 1.0),
+                "finite": all(st["o_finite"] and st["f_finite"] for st in stats), "seconds": wall,
+                "pair_steps": sum(st["pair_steps"] for st in stats), "workers": len(self.dirs)}
+

@@ -13,6 +13,13 @@ compares them with the oracle.  It writes stats.json: the oracle's wall time,
 the token-heads it ran, and max |gpu - ref| and max |ref| for o and the final
 state; with "keep_o_ref" in meta.json it also writes the oracle's o as
 o_ref.npy.
+
+Kind "decode": the worker's slice of (sequence, head) pairs over a run of
+decode steps.  state0 [n, H, d_k, d_v] is the state before the first step;
+step s has its own files <name>_<s> for q, k, v, decay (log alpha), beta and
+o_gpu ([n, H, .]); fin_gpu is the state after the last step.  stats.json
+then holds, per step, max |gpu - ref| and max |ref| of o, and the same for
+the final state.
 """
 import json
 import os
@@ -35,9 +42,31 @@ def load(d: str, name: str):
     return None
 
 
+def decode(d: str, meta: dict):
+    S = load(d, "state0").astype(np.float64)
+    o_err, o_ref_max, o_finite = [], [], True
+    t0 = time.perf_counter()
+    for s in range(meta["steps"]):
+        x = {n: load(d, f"{n}_{s}") for n in ("q", "k", "v", "decay", "beta", "o_gpu")}
+        o, S = oracle.kda_decode_step(x["q"], x["k"], x["v"], x["decay"], x["beta"], S)
+        o_err.append(float(np.abs(x["o_gpu"].astype(np.float64) - o).max()))
+        o_ref_max.append(float(np.abs(o).max()))
+        o_finite = o_finite and bool(np.isfinite(x["o_gpu"]).all())
+    seconds = time.perf_counter() - t0
+    f_gpu = load(d, "fin_gpu")
+    return {"seconds": seconds, "pair_steps": int(S.shape[0] * S.shape[1] * meta["steps"]),
+            "o_err_max": o_err, "o_ref_max": o_ref_max,
+            "f_err_max": float(np.abs(f_gpu.astype(np.float64) - S).max()), "f_ref_max": float(np.abs(S).max()),
+            "o_finite": o_finite, "f_finite": bool(np.isfinite(f_gpu).all())}
+
+
 def main(d: str):
     with open(os.path.join(d, "meta.json")) as f:
         meta = json.load(f)
+    if meta["kind"] == "decode":
+        with open(os.path.join(d, "stats.json"), "w") as f:
+            json.dump(decode(d, meta), f)
+        return
     q, k, v, decay, beta = (load(d, n) for n in ("q", "k", "v", "decay", "beta"))
     init, cu, a_log = load(d, "init_state"), load(d, "cu_seqlens"), load(d, "a_log")
     t0 = time.perf_counter()
