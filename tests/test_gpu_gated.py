@@ -72,9 +72,10 @@ def test_gated_varlen_all_heads():
     check_all_heads(x, "packed varlen")
 
 
-def test_gated_long_64k_four_heads():
+@pytest.mark.timeout(600)
+def test_gated_long_64k_all_heads():
     x = ki.gated_inputs([65536], H=96, d=128, dtype="bf16", seed=14, device=device())
-    check_prefill(x, "bf16", heads=np.random.default_rng(14).choice(96, 4, replace=False), what="64K")
+    check_all_heads(x, "64K")
 
 
 @pytest.mark.parametrize("dtype,d,d_v", [("bf16", 128, 128), ("f32", 64, 128), ("bf16", 128, 64)])
