@@ -668,6 +668,73 @@ def record_counters(pmc_dir: str, copy_gib: float):
     print(f"wrote {os.path.relpath(path, ROOT)}")
 
 
+def _smi_power_clocks():
+    """One `amd-smi metric -p -c` reading: (socket power in W, [gfx clocks in MHz]), or None."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                           timeout=10)
+        j = json.loads(r.stdout)
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+    def find(o):      # the first object holding both the power and the clock readings
+        if isinstance(o, dict):
+            if "power" in o and "clock" in o:
+                return o
+            o = list(o.values())
+        if isinstance(o, list):
+            for v in o:
+                r = find(v)
+                if r is not None:
+                    return r
+        return None
+    g = find(j)
+    try:
+        watts = float(g["power"]["socket_power"]["value"])
+        clocks = [float(v["clk"]["value"]) for k, v in g["clock"].items()
+                  if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+    except (KeyError, TypeError, ValueError):
+        return None
+    return watts, clocks
+
+
+def sample_power(dev, x, o, fin, seconds):
+    """Socket power and shader clocks while the prefill runs back to back for `seconds`, read with
+    amd-smi every 0.3 s on a second thread (the first 0.5 s, while the clocks ramp, is dropped)."""
+    import threading
+    import torch
+    from gated_delta_rule_09_amd import kda_chunk_prefill
+    reads, stop = [], threading.Event()
+
+    def sampler(t0):
+        while not stop.is_set():
+            r = _smi_power_clocks()
+            if r is not None and time.perf_counter() - t0 > 0.5:
+                reads.append(r)
+            stop.wait(0.3)
+
+    idle = _smi_power_clocks()
+    t0 = time.perf_counter()
+    th = threading.Thread(target=sampler, args=(t0,), daemon=True)
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            kda_chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.init_state, None, o=o, final_state=fin)
+        torch.cuda.synchronize()
+        n += 20
+    wall = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    if not reads:
+        return {"error": "amd-smi gave no reading"}
+    watts = sorted(r[0] for r in reads)
+    clocks = sorted(c for r in reads for c in r[1])
+    return {"prefills": n, "ms_per_prefill": round(1e3 * wall / n, 4), "readings": len(reads),
+            "socket_power_w_median": watts[len(watts) // 2], "socket_power_w_range": [watts[0], watts[-1]],
+            "gfx_clock_mhz_median": clocks[len(clocks) // 2], "gfx_clock_mhz_range": [clocks[0], clocks[-1]],
+            "idle_socket_power_w": None if idle is None else idle[0]}
+
+
 def time_stream_reference(dev, stream, gib=3.0, reps=10):
     """Plain streaming rates of this GPU, as context for the HBM fractions: torch's own in-place scale
     (read:write 1:1), add (2:1), fill (write only) and copy over fp32 buffers of `gib` GiB each.
@@ -721,6 +788,9 @@ def main():
                          "split at that length with 12 heads")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device-to-device copy of this many GiB (counter calibration)")
+    ap.add_argument("--power-seconds", type=float, default=0.0,
+                    help="also run the prefill back to back for this many seconds while amd-smi reads the "
+                         "socket power and shader clocks")
     ap.add_argument("--stream-reference", action="store_true",
                     help="also time torch's plain streaming ops (in-place scale, copy, add, fill) on 3 GiB buffers")
     ap.add_argument("--record-counters", metavar="PMC_DIR",
@@ -832,6 +902,8 @@ def main():
                                 "traffic": measured_traffic("decode", dec_ms),
                                 "kernel": "decode_kernel", "algorithmic_bytes_per_launch": dec_bytes}},
     }
+    if args.power_seconds > 0:
+        res["power"] = sample_power(dev, x, o, fin, args.power_seconds)
     if not args.no_varlen:
         res["varlen"] = time_varlen(args, dev, stream, ki, kda_chunk_prefill)
     if not args.no_gated:

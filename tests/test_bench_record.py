@@ -111,3 +111,24 @@ def test_record_from_synthetic_passes(tmp_path, monkeypatch):
     assert p["code_digest"] == bench.kernel_digest("prefill")
     assert set(rec) >= {"prefill", "decode", "epilogue", "epilogue_after_prefill", "prefill_gated",
                         "decode_epilogue", "prologue", "decode_fused", "calibration"}
+
+
+def test_power_reading_parser(monkeypatch):
+    """bench.py's amd-smi reading finds the socket power and the per-XCD shader
+    clocks wherever the JSON nests them, and gives None when they are absent."""
+    import subprocess
+
+    def fake(out):
+        class R:
+            stdout = json.dumps(out)
+        monkeypatch.setattr(subprocess, "run", lambda *a, **k: R())
+
+    reading = {"gpu": 0, "power": {"socket_power": {"value": 1318, "unit": "W"}, "gfx_voltage": "N/A"},
+               "clock": {"gfx_0": {"clk": {"value": 2352, "unit": "MHz"}}, "gfx_1": {"clk": {"value": 2309}},
+                         "mem_0": {"clk": {"value": 1900}}, "fclk_0": {"clk": "N/A"}}}
+    fake([reading])
+    assert bench._smi_power_clocks() == (1318.0, [2352.0, 2309.0])
+    fake({"gpu_data": [reading]})
+    assert bench._smi_power_clocks() == (1318.0, [2352.0, 2309.0])
+    fake({"other": 1})
+    assert bench._smi_power_clocks() is None
